@@ -1,0 +1,345 @@
+"""Seeded synthetic inputs for attention over a paged KV cache.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the HIP path and the CPU oracle can be fed from
+it without sharing any of the method.
+
+Shapes follow the pages' workloads: Llama-3-8B (32 query heads, 8 KV heads,
+head_dim 128) and Llama-2-70B (64 query heads in 8 groups) — "LLaMA inference
+performance: structure and source", section 2.1 (MHA to GQA); 16-token blocks
+by default — "Llama 4 inference doubling (FlashAttention-3 + PagedAttention +
+vLLM)", sections 3.1 and 3.2.
+
+Conventions of the arrays returned (all NumPy, host memory):
+  * bf16 tensors are ``uint16`` bit patterns (round-to-nearest-even of fp32
+    draws); fp32 tensors are ``float32``.
+  * KV pools are ``[num_blocks, H_kv, block_size, head_dim]``.
+  * ``block_tables`` is int32 ``[B, max_blocks_per_seq]``, padded with -1.
+  * Pool memory that no sequence uses (free blocks and the tail slots after a
+    sequence's last token) holds NaN, so that any over-read shows up.
+  * ``slot_mapping`` entries are ``block_id * block_size + offset``; -1 skips.
+
+Draw order is fixed per case: context lengths, block permutation, history
+K/V, q, then the new tokens' k/v.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# --------------------------------------------------------------------------
+# dtype helpers (bit-level, no arithmetic of the method)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, nearest-even, returned as uint16 bits.
+
+    Inputs must be finite (the generator never draws NaN/Inf).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def nan_value(dtype: str):
+    return BF16_NAN if dtype == BF16 else np.float32(np.nan)
+
+
+def storage_dtype(dtype: str):
+    return np.uint16 if dtype == BF16 else np.float32
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str, dist: str = "normal",
+          chunk: int = 1 << 24) -> np.ndarray:
+    """iid draws in float32, stored in ``dtype`` (bf16 via RNE), chunked."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=storage_dtype(dtype))
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        if dist == "normal":
+            x = rng.standard_normal(m, dtype=np.float32)
+        elif dist == "uniform":
+            x = rng.uniform(-1.0, 1.0, m).astype(np.float32)
+        else:
+            raise ValueError(dist)
+        out[s:s + m] = f32_to_bf16_bits(x) if dtype == BF16 else x
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------
+# Decode workloads
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    ctx_min: int = 0
+    ctx_max: int = 0
+    ctx_fixed: Optional[tuple] = None     # explicit context lengths
+    pool_factor: float = 1.25             # pool = ceil(factor * needed)
+    num_blocks: Optional[int] = None      # explicit pool size
+    max_blocks_per_seq: Optional[int] = None
+    share_group: int = 0                  # sequences per prefix-sharing group
+    share_blocks: int = 0                 # shared leading blocks per group
+    write_new_token: bool = True          # last position arrives via paged_kv_write
+    v_dist: str = "normal"
+    partition_size: int = 0               # 0 = single pass; else split-KV
+    pool_copies: int = 1                  # bench: independent copies (defeat MALL)
+
+
+@dataclass
+class DecodeCase:
+    spec: DecodeSpec
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    k_new: np.ndarray          # [T_new, H_kv, d]
+    v_new: np.ndarray
+    slot_mapping: np.ndarray   # [T_new] int32
+    scale: float
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+
+def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, Hq, Hkv, d, bs = (spec.batch, spec.num_q_heads, spec.num_kv_heads,
+                         spec.head_dim, spec.block_size)
+    # 1. context lengths
+    if spec.ctx_fixed is not None:
+        ctx = np.asarray(spec.ctx_fixed, dtype=np.int32)
+        assert ctx.shape == (B,)
+    else:
+        ctx = rng.integers(spec.ctx_min, spec.ctx_max + 1, size=B).astype(np.int32)
+    nblk = (ctx.astype(np.int64) + bs - 1) // bs
+    mbps = spec.max_blocks_per_seq or int(max(1, nblk.max()))
+    assert nblk.max() <= mbps
+
+    # 2. block ids: shared prefixes first, then private blocks, all permuted
+    if spec.share_group:
+        assert B % spec.share_group == 0
+        n_groups = B // spec.share_group
+        assert (nblk >= spec.share_blocks).all()
+        needed = n_groups * spec.share_blocks + int((nblk - spec.share_blocks).sum())
+    else:
+        needed = int(nblk.sum())
+    NB = spec.num_blocks or int(math.ceil(spec.pool_factor * needed))
+    assert NB >= needed
+    perm = rng.permutation(NB).astype(np.int32)
+    tables = np.full((B, mbps), -1, dtype=np.int32)
+    cursor = 0
+    if spec.share_group:
+        shared = []
+        for gi in range(B // spec.share_group):
+            shared.append(perm[cursor:cursor + spec.share_blocks])
+            cursor += spec.share_blocks
+        for b in range(B):
+            tables[b, :spec.share_blocks] = shared[b // spec.share_group]
+            n_priv = int(nblk[b]) - spec.share_blocks
+            tables[b, spec.share_blocks:spec.share_blocks + n_priv] = perm[cursor:cursor + n_priv]
+            cursor += n_priv
+    else:
+        for b in range(B):
+            n = int(nblk[b])
+            tables[b, :n] = perm[cursor:cursor + n]
+            cursor += n
+
+    # 3. history K/V: iid draws over the whole pool, then NaN where unused
+    shape = (NB, Hkv, bs, d)
+    k_cache = _draw(rng, shape, spec.dtype, "normal")
+    v_cache = _draw(rng, shape, spec.dtype, spec.v_dist)
+    used = np.zeros((NB, bs), dtype=bool)
+    for b in range(B):
+        n = int(ctx[b])
+        # positions that hold history (the new token, if any, arrives by write)
+        hist = n - 1 if (spec.write_new_token and n > 0) else n
+        for p0 in range(0, hist, bs):
+            blk = tables[b, p0 // bs]
+            used[blk, :min(bs, hist - p0)] = True
+    nanv = nan_value(spec.dtype)
+    mask = ~used  # [NB, bs]
+    k_cache.transpose(0, 2, 1, 3)[mask] = nanv
+    v_cache.transpose(0, 2, 1, 3)[mask] = nanv
+
+    # 4. queries
+    q = _draw(rng, (B, Hq, d), spec.dtype, "normal")
+
+    # 5. the new token of each sequence (position ctx-1), written by slot
+    if spec.write_new_token:
+        k_new = _draw(rng, (B, Hkv, d), spec.dtype, "normal")
+        v_new = _draw(rng, (B, Hkv, d), spec.dtype, spec.v_dist)
+        slots = np.full(B, -1, dtype=np.int32)
+        for b in range(B):
+            p = int(ctx[b]) - 1
+            if p >= 0:
+                slots[b] = tables[b, p // bs] * bs + p % bs
+    else:
+        k_new = np.zeros((0, Hkv, d), dtype=storage_dtype(spec.dtype))
+        v_new = k_new.copy()
+        slots = np.zeros(0, dtype=np.int32)
+
+    return DecodeCase(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache,
+                      block_tables=tables, context_lens=ctx, k_new=k_new,
+                      v_new=v_new, slot_mapping=slots, scale=1.0 / math.sqrt(d))
+
+
+# --------------------------------------------------------------------------
+# Prefill workloads
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    len_min: int = 0
+    len_max: int = 0
+    lens_fixed: Optional[tuple] = None
+    block_size: int = 16          # paged write-through of the prompt K/V
+    pool_factor: float = 1.25
+
+
+@dataclass
+class PrefillCase:
+    spec: PrefillSpec
+    q: np.ndarray            # [T, H_q, d]
+    k: np.ndarray            # [T, H_kv, d]
+    v: np.ndarray
+    cu_seqlens: np.ndarray   # [S+1] int32
+    scale: float
+    # paged write-through of k/v
+    slot_mapping: np.ndarray  # [T] int32
+    block_tables: np.ndarray  # [S, max_blocks]
+    num_blocks: int
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def max_seqlen(self) -> int:
+        lens = np.diff(self.cu_seqlens)
+        return int(lens.max()) if lens.size else 0
+
+
+def make_prefill_case(spec: PrefillSpec, seed: int) -> PrefillCase:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, Hq, Hkv, d, bs = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads,
+                         spec.head_dim, spec.block_size)
+    if spec.lens_fixed is not None:
+        lens = np.asarray(spec.lens_fixed, dtype=np.int64)
+        assert lens.shape == (S,)
+    else:
+        lens = rng.integers(spec.len_min, spec.len_max + 1, size=S).astype(np.int64)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    T = int(cu[-1])
+    nblk = (lens + bs - 1) // bs
+    needed = int(nblk.sum())
+    NB = int(math.ceil(spec.pool_factor * needed)) if needed else 1
+    perm = rng.permutation(NB).astype(np.int32)
+    mbps = int(max(1, nblk.max() if nblk.size else 1))
+    tables = np.full((S, mbps), -1, dtype=np.int32)
+    slots = np.empty(T, dtype=np.int32)
+    cursor = 0
+    for s in range(S):
+        n = int(nblk[s])
+        tables[s, :n] = perm[cursor:cursor + n]
+        cursor += n
+        for i in range(int(lens[s])):
+            slots[cu[s] + i] = tables[s, i // bs] * bs + i % bs
+    q = _draw(rng, (T, Hq, d), spec.dtype)
+    k = _draw(rng, (T, Hkv, d), spec.dtype)
+    v = _draw(rng, (T, Hkv, d), spec.dtype)
+    return PrefillCase(spec=spec, q=q, k=k, v=v, cu_seqlens=cu,
+                       scale=1.0 / math.sqrt(d), slot_mapping=slots,
+                       block_tables=tables, num_blocks=NB)
+
+
+def empty_pool(num_blocks: int, num_kv_heads: int, block_size: int,
+               head_dim: int, dtype: str) -> np.ndarray:
+    """A pool whose every slot holds NaN (nothing written yet)."""
+    return np.full((num_blocks, num_kv_heads, block_size, head_dim),
+                   nan_value(dtype), dtype=storage_dtype(dtype))
+
+
+# --------------------------------------------------------------------------
+# The five workloads (seed = 1000 + index)
+# --------------------------------------------------------------------------
+TINY_DECODE_F32 = DecodeSpec(
+    name="tiny_paged_decode_f32", dtype=F32, batch=4, num_q_heads=4,
+    num_kv_heads=2, head_dim=64, block_size=16, ctx_fixed=(1, 17, 33, 64),
+    num_blocks=32, max_blocks_per_seq=4, partition_size=0)
+
+LLAMA3_8B_DECODE = DecodeSpec(
+    name="llama3_8b_paged_decode_bf16", dtype=BF16, batch=64, num_q_heads=32,
+    num_kv_heads=8, head_dim=128, block_size=16, ctx_min=128, ctx_max=2048,
+    max_blocks_per_seq=128, partition_size=256)
+
+LLAMA3_8B_PREFILL = PrefillSpec(
+    name="llama3_8b_varlen_causal_prefill_bf16", dtype=BF16, num_seqs=16,
+    num_q_heads=32, num_kv_heads=8, head_dim=128, len_min=64, len_max=2048,
+    block_size=16)
+
+LLAMA2_70B_PREFIX_DECODE = DecodeSpec(
+    name="llama2_70b_prefix_shared_decode_bf16", dtype=BF16, batch=256,
+    num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+    ctx_min=512, ctx_max=4096, max_blocks_per_seq=128, share_group=8,
+    share_blocks=16, write_new_token=False, partition_size=512)
+
+LONG_CONTEXT_SPLIT_DECODE = DecodeSpec(
+    name="long_context_split_kv_decode_bf16", dtype=BF16, batch=4,
+    num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+    ctx_fixed=(131072,) * 4, num_blocks=40960, max_blocks_per_seq=8192,
+    write_new_token=False, v_dist="uniform", partition_size=512)
+
+CONFIGS = {
+    1: TINY_DECODE_F32,
+    2: LLAMA3_8B_DECODE,
+    3: LLAMA3_8B_PREFILL,
+    4: LLAMA2_70B_PREFIX_DECODE,
+    5: LONG_CONTEXT_SPLIT_DECODE,
+}
+
+
+def seed_for(config_index: int) -> int:
+    return 1000 + config_index
+
+
+def make_case(config_index: int, seed: Optional[int] = None, **overrides):
+    """Build workload ``config_index`` (1..5), optionally shrunk by overrides."""
+    spec = CONFIGS[config_index]
+    if overrides:
+        spec = replace(spec, **overrides)
+    s = seed_for(config_index) if seed is None else seed
+    if isinstance(spec, PrefillSpec):
+        return make_prefill_case(spec, s)
+    return make_decode_case(spec, s)

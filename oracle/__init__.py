@@ -1,0 +1,9 @@
+"""CPU oracle for attention over a paged KV cache (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP path.
+"""
+from .attention import (  # noqa: F401
+    BF16, F32, attend, decode, decode_one, decode_partitions, gather,
+    group_of, kv_write, num_partitions, prefill, reduce_partitions, upcast,
+)

@@ -1,0 +1,138 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant swaps one oracle function for a copy with one plausible slip (a
+wrong group map, a dropped scale, a log in the wrong base, a transposed
+index, an off-by-one in the mask or the context), then runs the pins of
+test_oracle_pins.py against it and expects at least one to fail.  The real
+oracle is restored after each case.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oa
+from tests import test_oracle_pins as pins
+
+
+def _attend_no_scale(q, K, V, scale):
+    return oa.__dict__["_orig_attend"](q, K, V, 1.0)
+
+
+def _attend_log2(q, K, V, scale):
+    out, lse, p = oa.__dict__["_orig_attend"](q, K, V, scale)
+    return out, lse / math.log(2.0), p
+
+
+def _attend_drop_last_key(q, K, V, scale):
+    if K.shape[0] > 1:
+        K, V = K[:-1], V[:-1]
+    return oa.__dict__["_orig_attend"](q, K, V, scale)
+
+
+def _group_mod(h, num_q_heads, num_kv_heads):
+    return h % (num_q_heads // num_kv_heads)
+
+
+def _gather_swapped(pool, table_row, ctx, block_size):
+    rows = []
+    for p in range(int(ctx)):
+        blk = int(table_row[p % block_size]) if p % block_size < len(table_row) else 0
+        rows.append(pool[blk, :, p // block_size % block_size, :])
+    if not rows:
+        return np.zeros((0, pool.shape[1], pool.shape[3]), dtype=pool.dtype)
+    return np.stack(rows)
+
+
+def _kv_write_off_by_one(k_cache, v_cache, k, v, slot_mapping, block_size):
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    for t, s in enumerate(slot_mapping):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), block_size)
+        off = (off + 1) % block_size
+        kc[blk, :, off, :] = k[t]
+        vc[blk, :, off, :] = v[t]
+    return kc, vc
+
+
+def _prefill_mask(shift):
+    def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        out = np.zeros((T, Hq, d))
+        lse = np.full((T, Hq), -math.inf)
+        for s in range(len(cu_seqlens) - 1):
+            a, e = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+            L = e - a
+            if L <= 0:
+                continue
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                Q, K, V = (oa.upcast(q[a:e, h], dtype), oa.upcast(k[a:e, g], dtype),
+                           oa.upcast(v[a:e, g], dtype))
+                sc = scale * (Q @ K.T)
+                sc[np.triu(np.ones((L, L), bool), shift)] = -np.inf
+                m = sc.max(1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                w = np.exp(sc - m)
+                z = w.sum(1, keepdims=True)
+                out[a:e, h] = (w / z) @ V
+                lse[a:e, h] = (m + np.log(z))[:, 0]
+        return out, lse
+    return prefill
+
+
+def _reduce_counts_dead(part_out, part_lse, context_lens, partition_size):
+    B, Hq, P, d = part_out.shape
+    return oa.__dict__["_orig_reduce"](part_out, part_lse, np.full(B, P * partition_size), partition_size)
+
+
+MUTANTS = {
+    "group_map_h_mod_G": [("group_of", _group_mod)],
+    "dropped_scale": [("attend", _attend_no_scale)],
+    "lse_in_log2": [("attend", _attend_log2)],
+    "context_off_by_one": [("attend", _attend_drop_last_key)],
+    "gather_block_offset_swapped": [("gather", _gather_swapped)],
+    "write_offset_off_by_one": [("kv_write", _kv_write_off_by_one)],
+    "causal_mask_hides_diagonal": [("prefill", _prefill_mask(0))],
+    "causal_mask_leaks_next_key": [("prefill", _prefill_mask(2))],
+    "merge_counts_dead_partitions": [("reduce_partitions", _reduce_counts_dead)],
+}
+
+PIN_CALLS = [
+    lambda g: pins.test_golden_kv_write(g),
+    lambda g: pins.test_golden_attention_closed_form(g),
+    lambda g: pins.test_golden_causal_prefill(g),
+    lambda g: pins.test_golden_gqa_group_map(g),
+    lambda g: pins.test_golden_lse_merge(g),
+    lambda g: pins.test_decode_equals_unpaged_sdpa(4, 2, 64, 16, (1, 17, 33, 64)),
+    lambda g: pins.test_needle_picks_one_value(63),
+    lambda g: pins.test_single_key_returns_its_value(),
+    lambda g: pins.test_prefill_equals_dense_causal_sdpa(),
+    lambda g: pins.test_split_then_merge_equals_unsplit(48),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, golden_dir, monkeypatch):
+    monkeypatch.setitem(oa.__dict__, "_orig_attend", oa.attend)
+    monkeypatch.setitem(oa.__dict__, "_orig_reduce", oa.reduce_partitions)
+    for fn_name, repl in MUTANTS[name]:
+        monkeypatch.setattr(oa, fn_name, repl)
+        if hasattr(oracle, fn_name):
+            monkeypatch.setattr(oracle, fn_name, repl)
+    caught = 0
+    for call in PIN_CALLS:
+        try:
+            with np.errstate(all="ignore"):
+                call(golden_dir)
+        except (AssertionError, IndexError, ValueError):
+            caught += 1
+    assert caught >= 1, f"no pin caught mutant {name}"
+
+
+def test_unmutated_oracle_passes_every_pin(golden_dir):
+    for call in PIN_CALLS:
+        call(golden_dir)
