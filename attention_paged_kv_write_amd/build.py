@@ -1,0 +1,83 @@
+"""Build the HIP library ``libpaged_attn.so`` in-tree for gfx950.
+
+Each ``csrc/*.hip`` file is compiled to an object with hipcc and the objects
+are linked into one shared library next to this file.  Usage:
+``python -m attention_paged_kv_write_amd.build [--jobs N] [--verbose]``.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB_NAME = "libpaged_attn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from forming packed fp32 ops (v_pk_fma_f32 and friends)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src, verbose=False, extra=()):
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    warn = "\n".join(line for line in r.stderr.splitlines()
+                     if "packed-fp32-ops" not in line and line.strip())
+    return obj, warn
+
+
+def build(jobs: int = 8, verbose: bool = False, extra=()) -> str:
+    """Compile every HIP source and link the shared library; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        results = list(ex.map(lambda s: _compile(s, verbose, extra), srcs))
+    for obj, warn in results:
+        if warn and verbose:
+            print(warn, file=sys.stderr)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           *[o for o, _ in results]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    path = build(args.jobs, args.verbose)
+    print(path)
+
+
+if __name__ == "__main__":
+    main()

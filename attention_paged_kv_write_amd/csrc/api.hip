@@ -1,0 +1,222 @@
+// C ABI of the paged-attention library: argument validation, kernel choice and
+// launch on the caller's stream.  No allocation, no synchronisation, no host
+// read of device memory.  The declarations and their contracts are in
+// include/paged_attn.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "paged_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+int g_force_vector_path = 0;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for these arguments", what);
+  return fail(PA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+int esize(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return 1; }
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_set_option(int option, int value) {
+  if (option == PA_OPT_FORCE_VECTOR_PATH) {
+    g_force_vector_path = value != 0;
+    return ok();
+  }
+  return fail(PA_ERR_INVALID_ARG, "pa_set_option: unknown option %d", option);
+}
+
+int paged_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                   const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, pa_dtype dtype, void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "paged_kv_write: num_tokens < 0");
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "paged_kv_write: unknown dtype %d", (int)dtype);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "paged_kv_write: non-positive size");
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "paged_kv_write: num_blocks * block_size exceeds int32 slots");
+  if ((static_cast<int64_t>(head_dim) * esize(dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "paged_kv_write: head_dim * sizeof(dtype) must be a multiple of 16");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "paged_kv_write: null pointer");
+  pa::KvWriteArgs a;
+  a.k = static_cast<const pa::u32x4*>(k);
+  a.v = static_cast<const pa::u32x4*>(v);
+  a.k_cache = static_cast<pa::u32x4*>(k_cache);
+  a.v_cache = static_cast<pa::u32x4*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_chunks = head_dim * esize(dtype) / 16;
+  a.row_chunks = num_kv_heads * a.head_chunks;
+  a.block_size = block_size;
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  return launch_status(pa::launch_kv_write(a, static_cast<hipStream_t>(stream)), "paged_kv_write");
+}
+
+int paged_attention_decode(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                           int num_blocks, int partition_size, int max_context_len, float scale,
+                           pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode";
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be 0 or a multiple of block_size", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+  if (!(block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  if (!group_ok(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, num_q_heads / num_kv_heads);
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
+  int num_parts = 1;
+  if (partition_size > 0) {
+    if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
+    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+  } else if (!out || !lse) {
+    return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
+  }
+  pa::DecodeArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.num_partitions = num_parts;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * pa::kLog2e;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s)
+                                           : pa::launch_decode(a, dt, head_dim, s);
+  return launch_status(e, fn);
+}
+
+int paged_attention_reduce(void* out, float* lse, const float* part_out, const float* part_lse,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
+                           int partition_size, int max_partitions, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_reduce";
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0 || max_partitions <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+  if (static_cast<int64_t>(num_seqs) * num_q_heads > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (num_seqs == 0) return ok();
+  if (!out || !lse || !part_out || !part_lse || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::ReduceArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  return launch_status(pa::launch_reduce(a, dt, static_cast<hipStream_t>(stream)), fn);
+}
+
+int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
+                          int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                          pa_dtype dtype, void* stream) {
+  const char* fn = "varlen_causal_prefill";
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
+  if (max_seqlen > total_tokens) return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen > total_tokens", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+  if (!group_ok(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, num_q_heads / num_kv_heads);
+  if (static_cast<int64_t>(num_q_heads) * num_seqs > INT32_MAX || num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%s: too many sequences", fn);
+  if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return ok();
+  if (!out || !lse || !q || !k || !v || !cu_seqlens) return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::PrefillArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.max_seqlen = max_seqlen;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * pa::kLog2e;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = g_force_vector_path ? pa::launch_prefill_generic(a, dt, head_dim, s)
+                                           : pa::launch_prefill(a, dt, head_dim, s);
+  return launch_status(e, fn);
+}
+
+}  // extern "C"

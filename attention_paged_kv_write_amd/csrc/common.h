@@ -1,0 +1,105 @@
+// Device helpers shared by the kernels of the paged-attention library (gfx950).
+//
+// Wave64 throughout.  Cross-lane reductions use DPP inside a 16-lane row
+// (quad_perm, row_half_mirror, row_mirror), ds_swizzle across the two rows of
+// a 32-lane half, and ds_bpermute between the two halves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32 on raw bit patterns
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                         CTRL, 0xf, 0xf, false));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within 16
+
+// Lane i <- lane i ^ 16 (inside each 32-lane half): ds_swizzle bit mode,
+// and_mask 0x1f, or_mask 0, xor_mask 0x10.
+__device__ __forceinline__ float swz_xor16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+// Lane i <- lane i ^ 32.
+__device__ __forceinline__ float xchg_xor32(float x) {
+  const int src = (__lane_id() ^ 32) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
+}
+
+// Lane i <- lane i ^ m for any m in {1,...,32} (epilogue use).
+__device__ __forceinline__ float xchg_xor(float x, int m) {
+  const int src = (__lane_id() ^ m) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
+}
+
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// All-reduce over groups of W consecutive lanes (W in 1,2,4,8,16,32,64).
+template <int W, class Op>
+__device__ __forceinline__ float group_allreduce(float x, Op op) {
+  if constexpr (W >= 2) x = op(x, dpp_f32<kDppXor1>(x));
+  if constexpr (W >= 4) x = op(x, dpp_f32<kDppXor2>(x));
+  if constexpr (W >= 8) x = op(x, dpp_f32<kDppRowHalfMirror>(x));
+  if constexpr (W >= 16) x = op(x, dpp_f32<kDppRowMirror>(x));
+  if constexpr (W >= 32) x = op(x, swz_xor16(x));
+  if constexpr (W >= 64) x = op(x, xchg_xor32(x));
+  return x;
+}
+
+// All-reduce across the four 16-lane rows (lanes l, l^16, l^32, l^48).
+template <class Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+  x = op(x, swz_xor16(x));
+  x = op(x, xchg_xor32(x));
+  return x;
+}
+
+// exp2 that treats a -inf argument exactly (hardware v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace pa

@@ -1,0 +1,87 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Argument structs are passed to kernels by value; all pointers are device
+// pointers already validated on the host.
+#pragma once
+
+#include "common.h"
+
+namespace pa {
+
+struct KvWriteArgs {
+  const u32x4* k;        // [T, H_kv, d] as 16-byte chunks
+  const u32x4* v;
+  u32x4* k_cache;        // [NB, H_kv, bs, d] as 16-byte chunks
+  u32x4* v_cache;
+  const int32_t* slot_mapping;
+  int num_tokens;
+  int num_kv_heads;
+  int head_chunks;       // d * sizeof(T) / 16
+  int row_chunks;        // H_kv * head_chunks
+  int block_size;
+  int64_t num_slots;     // NB * bs
+};
+
+struct DecodeArgs {
+  void* out;             // [B, H_q, d] (T)        when partition_size == 0
+  float* lse;            // [B, H_q]               when partition_size == 0
+  float* part_out;       // [B, H_q, P, d]          when partition_size > 0
+  float* part_lse;       // [B, H_q, P]
+  const void* q;         // [B, H_q, d]
+  const void* k_cache;   // [NB, H_kv, bs, d]
+  const void* v_cache;
+  const int32_t* block_tables;  // [B, max_blocks_per_seq]
+  const int32_t* context_lens;  // [B]
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int partition_size;    // 0 = single pass
+  int num_partitions;    // partition dimension of part_* (1 when single pass)
+  int max_context_len;
+  float scale_log2;      // scale * log2(e)
+};
+
+struct ReduceArgs {
+  void* out;
+  float* lse;
+  const float* part_out;
+  const float* part_lse;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_q_heads;
+  int head_dim;
+  int partition_size;
+  int max_partitions;
+};
+
+struct PrefillArgs {
+  void* out;             // [T, H_q, d]
+  float* lse;            // [T, H_q]
+  const void* q;         // [T, H_q, d]
+  const void* k;         // [T, H_kv, d]
+  const void* v;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int total_tokens;
+  int max_seqlen;
+  int num_q_heads;
+  int num_kv_heads;
+  float scale_log2;
+};
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+// Returns hipErrorNotSupported when no kernel instance covers the shape.
+hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, DType dt, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
+
+// The vector-ALU kernels alone (also the path for shapes without an MFMA kernel).
+hipError_t launch_decode_generic(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
+
+}  // namespace pa

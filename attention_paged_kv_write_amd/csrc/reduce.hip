@@ -1,0 +1,103 @@
+// paged_attention_reduce: merge split-KV partitions by log-sum-exp.
+//
+// Each partition's (out, lse) pair is an exact summary of its keys: with
+// M = max lse and w = exp(lse - M) the merged output is sum w*out / sum w and
+// the merged lse is M + log(sum w).  The LSE output of the varlen call
+// ("Llama 4 inference doubling (FlashAttention-3 + PagedAttention + vLLM)",
+// section 2.4) is what makes the merge exact.
+//
+// One workgroup per (sequence, query head).  Pass 1 finds M; pass 2 turns a
+// chunk of partition lse values into weights held in LDS; pass 3 streams the
+// partition outputs (each wave takes every fourth partition, each lane a pair
+// of dims, 8 partitions in flight per wave) and the four waves meet in LDS.
+#include "kernels.h"
+
+namespace pa {
+
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  constexpr int DPL = D / 64;  // dims per lane
+  constexpr int CHUNK = 1024;
+  __shared__ float sm_w[CHUNK];
+  __shared__ float sm_red[4];
+  __shared__ float sm_acc[4][D];
+
+  const size_t row = blockIdx.x;  // b * H_q + h
+  const int b = static_cast<int>(row / a.num_q_heads);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t ctx = max(a.context_lens[b], 0);
+  const int64_t live = (ctx + a.partition_size - 1) / a.partition_size;
+  const int n = static_cast<int>(min<int64_t>(live, a.max_partitions));
+  const float* lse_row = a.part_lse + row * a.max_partitions;
+  const float* out_row = a.part_out + row * a.max_partitions * D;
+
+  float mx = kNegInf;
+  for (int i = tid; i < n; i += 256) mx = fmaxf(mx, lse_row[i]);
+  mx = group_allreduce<64>(mx, OpMax());
+  if (lane == 0) sm_red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+  __syncthreads();
+
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (M != kNegInf) {
+    for (int c0 = 0; c0 < n; c0 += CHUNK) {
+      const int cn = min(CHUNK, n - c0);
+      for (int i = tid; i < cn; i += 256) {
+        const float w = fast_exp2((lse_row[c0 + i] - M) * kLog2e);
+        sm_w[i] = w;
+        wsum += w;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int i = wave; i < cn; i += 4) {
+        const float w = sm_w[i];
+        const float* o = out_row + static_cast<size_t>(c0 + i) * D + lane * DPL;
+        if constexpr (DPL == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(o);
+          acc[0] = fmaf(w, v.x, acc[0]);
+          acc[1] = fmaf(w, v.y, acc[1]);
+        } else {
+          acc[0] = fmaf(w, o[0], acc[0]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  wsum = group_allreduce<64>(wsum, OpSum());
+  if (lane == 0) sm_red[wave] = wsum;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) sm_acc[wave][lane * DPL + e] = acc[e];
+  __syncthreads();
+  const float W = sm_red[0] + sm_red[1] + sm_red[2] + sm_red[3];
+  for (int d = tid; d < D; d += 256) {
+    float o = 0.f;
+    if (M != kNegInf) o = (sm_acc[0][d] + sm_acc[1][d] + sm_acc[2][d] + sm_acc[3][d]) / W;
+    if constexpr (BF) {
+      static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16_bits(o);
+    } else {
+      static_cast<float*>(a.out)[row * D + d] = o;
+    }
+  }
+  if (tid == 0) a.lse[row] = (M != kNegInf) ? M + __log2f(W) * kLn2 : kNegInf;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, DType dt, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.num_seqs) * a.num_q_heads));
+  if (a.num_seqs == 0) return hipSuccess;
+  if (dt == DType::BF16) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((reduce_kernel<true, 128>), grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((reduce_kernel<true, 64>), grid, dim3(256), 0, s, a);
+    else return hipErrorNotSupported;
+  } else {
+    if (a.head_dim == 128) hipLaunchKernelGGL((reduce_kernel<false, 128>), grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((reduce_kernel<false, 64>), grid, dim3(256), 0, s, a);
+    else return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,233 @@
+"""ctypes binding over the C ABI of ``libpaged_attn.so`` (include/paged_attn.h).
+
+Argument marshalling only: each function checks dtypes, shapes, contiguity and
+device of torch tensors, allocates outputs the caller did not pass (torch is
+the memory allocator), and hands raw device pointers plus the current HIP
+stream to the C call of the same name.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  If the library is missing or
+fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+
+PA_F32, PA_BF16 = 0, 1
+PA_OPT_FORCE_VECTOR_PATH = 1
+EXPORTED_SYMBOLS = (
+    "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
+    "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
+)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[code {code}] {message}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the shared library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not found at {path}; build it with "
+            "`python -m attention_paged_kv_write_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.pa_abi_version.restype = i32
+    lib.pa_abi_version.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_set_option.restype = i32
+    lib.pa_set_option.argtypes = [i32, i32]
+    lib.paged_kv_write.restype = i32
+    lib.paged_kv_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.paged_attention_decode.restype = i32
+    lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                           f32, i32, vp]
+    lib.paged_attention_reduce.restype = i32
+    lib.paged_attention_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.varlen_causal_prefill.restype = i32
+    lib.varlen_causal_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          f32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = _lib.pa_last_error().decode() if _lib is not None else ""
+        raise PagedAttnError(rc, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def set_force_vector_path(on: bool) -> None:
+    """Route decode/prefill to the vector-ALU kernels (cross-checking aid)."""
+    lib = load_library()
+    _check(lib.pa_set_option(PA_OPT_FORCE_VECTOR_PATH, int(bool(on))))
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Scatter k/v [T, H_kv, d] into the pools [NB, H_kv, bs, d] by slot (in place)."""
+    lib = load_library()
+    dt = _dtype_code(k)
+    for name, t in (("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != k.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != k dtype {k.dtype}")
+    pk = _dev(k, "k", ndim=3)
+    pv = _dev(v, "v", ndim=3)
+    pkc = _dev(k_cache, "k_cache", ndim=4)
+    pvc = _dev(v_cache, "v_cache", ndim=4)
+    ps = _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    T, H, d = k.shape
+    NB, H2, bs, d2 = k_cache.shape
+    if v.shape != k.shape or v_cache.shape != k_cache.shape or H2 != H or d2 != d:
+        raise ValueError("paged_kv_write: inconsistent shapes")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("paged_kv_write: slot_mapping length != num_tokens")
+    _check(lib.paged_kv_write(pk, pv, pkc, pvc, ps, T, H, d, bs, NB, dt, _stream(k)))
+
+
+def num_partitions(max_context_len: int, partition_size: int) -> int:
+    return max(1, -(-int(max_context_len) // int(partition_size)))
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: Optional[float] = None,
+                           partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           part_out: Optional[torch.Tensor] = None,
+                           part_lse: Optional[torch.Tensor] = None
+                           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """PagedAttention decode.  Returns (out, lse), or (part_out, part_lse) when split."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("paged_attention_decode: inconsistent q / cache shapes or dtypes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_attention_decode: block_tables / context_lens shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pq = _dev(q, "q", ndim=3)
+    pkc = _dev(k_cache, "k_cache", ndim=4)
+    pvc = _dev(v_cache, "v_cache", ndim=4)
+    pbt = _dev(block_tables, "block_tables", torch.int32, 2)
+    pcl = _dev(context_lens, "context_lens", torch.int32, 1)
+    po = pl = ppo = ppl = None
+    if partition_size > 0:
+        P = num_partitions(max_context_len, partition_size)
+        if part_out is None:
+            part_out = torch.empty((B, Hq, P, d), dtype=torch.float32, device=q.device)
+        if part_lse is None:
+            part_lse = torch.empty((B, Hq, P), dtype=torch.float32, device=q.device)
+        if part_out.shape != (B, Hq, P, d) or part_lse.shape != (B, Hq, P):
+            raise ValueError("paged_attention_decode: part_out/part_lse shape")
+        ppo = _dev(part_out, "part_out", torch.float32)
+        ppl = _dev(part_lse, "part_lse", torch.float32)
+    else:
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        if out.shape != q.shape or lse.shape != (B, Hq):
+            raise ValueError("paged_attention_decode: out/lse shape")
+        po = _dev(out, "out", q.dtype)
+        pl = _dev(lse, "lse", torch.float32)
+    _check(lib.paged_attention_decode(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
+                                      block_tables.shape[1], NB, int(partition_size),
+                                      int(max_context_len), float(scale), dt, _stream(q)))
+    if partition_size > 0:
+        return part_out, part_lse
+    return out, lse
+
+
+def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
+                           context_lens: torch.Tensor, partition_size: int,
+                           out_dtype: torch.dtype = torch.bfloat16,
+                           out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Log-sum-exp merge of split-KV partitions -> (out [B, H_q, d], lse [B, H_q])."""
+    lib = load_library()
+    B, Hq, P, d = part_out.shape
+    if part_lse.shape != (B, Hq, P) or context_lens.shape != (B,):
+        raise ValueError("paged_attention_reduce: shapes")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=part_out.device)
+    dt = _dtype_code(out)
+    _check(lib.paged_attention_reduce(_dev(out, "out", ndim=3), _dev(lse, "lse", torch.float32, 2),
+                                      _dev(part_out, "part_out", torch.float32, 4),
+                                      _dev(part_lse, "part_lse", torch.float32, 3),
+                                      _dev(context_lens, "context_lens", torch.int32, 1),
+                                      B, Hq, d, int(partition_size), P, dt, _stream(part_out)))
+    return out, lse
+
+
+def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          cu_seqlens: torch.Tensor, max_seqlen: int,
+                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal attention over sequences packed by cu_seqlens -> (out [T,H_q,d], lse [T,H_q])."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    T, Hq, d = q.shape
+    T2, Hkv, d2 = k.shape
+    if T2 != T or d2 != d or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("varlen_causal_prefill: inconsistent q/k/v")
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("varlen_causal_prefill: cu_seqlens must be [num_seqs + 1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.varlen_causal_prefill(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
+                                     _dev(q, "q", ndim=3), _dev(k, "k", ndim=3), _dev(v, "v", ndim=3),
+                                     _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
+                                     cu_seqlens.shape[0] - 1, T, int(max_seqlen), Hq, Hkv, d,
+                                     float(scale), dt, _stream(q)))
+    return out, lse

@@ -1,0 +1,277 @@
+"""Benchmark: attention over a paged KV cache on one MI355X.
+
+One step = the decode hot path on the Llama-3-8B-shaped workload (64
+sequences, 32 query / 8 KV heads, head_dim 128, 16-token blocks, contexts
+uniform in [128, 2048], shuffled pool 1.25x the need): paged_kv_write of the
+64 new tokens, split-KV paged_attention_decode (256-token partitions), and
+paged_attention_reduce.  The headline value is KV-cache bytes streamed per
+second (sum of context lengths x 8 KV heads x (K + V) x 128 x 2 bytes per step).
+
+Inputs are resident in HBM before timing.  R independent copies of the pools,
+tables and queries are rotated so the 256 MB Infinity Cache cannot serve one
+step's KV from the previous step.  The varlen causal prefill on the
+Llama-3-8B varlen workload (16 sequences, lengths uniform in [64, 2048]) is
+timed as a secondary figure (TFLOP/s over unmasked query-key pairs).
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV GB/s (% HBM peak); varlen prefill TFLOP/s; Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+DECODE_SOURCES = ("attention_paged_kv_write_amd/csrc/decode.hip",
+                  "attention_paged_kv_write_amd/csrc/common.h",
+                  "attention_paged_kv_write_amd/csrc/kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(bytes_per_launch_alg):
+    """HBM bytes per decode launch from committed rocprofv3 counters, if the
+    decode kernel source is unchanged since they were taken; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != source_digest(DECODE_SOURCES):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition-size", type=int, default=256)
+    ap.add_argument("--copies", type=int, default=3, help="independent input copies rotated per step")
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from attention_paged_kv_write_amd import ops
+    from attention_paged_kv_write_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    ops.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # ------------------------------------------------------------------ decode
+    t0 = time.perf_counter()
+    case = wl.make_case(2)
+    spec = case.spec
+    log(f"decode workload generated in {time.perf_counter() - t0:.1f}s: "
+        f"NB={case.num_blocks} sum(ctx)={int(case.context_lens.sum())}")
+    B, Hq, Hkv, d, bs = spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    ps = args.partition_size
+    maxctx = case.max_context_len
+    P = ops.num_partitions(maxctx, ps)
+    copies = []
+    for _ in range(max(1, args.copies)):
+        copies.append(dict(q=up(case.q), kc=up(case.k_cache), vc=up(case.v_cache),
+                           bt=up(case.block_tables), cl=up(case.context_lens),
+                           kn=up(case.k_new), vn=up(case.v_new), slots=up(case.slot_mapping),
+                           po=torch.empty((B, Hq, P, d), dtype=torch.float32, device=dev),
+                           pl=torch.empty((B, Hq, P), dtype=torch.float32, device=dev),
+                           out=torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev),
+                           lse=torch.empty((B, Hq), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(c, ev=None):
+        ops.paged_kv_write(c["kn"], c["vn"], c["kc"], c["vc"], c["slots"])
+        if ev is not None:
+            ev[0].record(stream)
+        ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], maxctx, case.scale, ps,
+                                   part_out=c["po"], part_lse=c["pl"])
+        if ev is not None:
+            ev[1].record(stream)
+        ops.paged_attention_reduce(c["po"], c["pl"], c["cl"], ps, out=c["out"], lse=c["lse"])
+
+    for i in range(args.warmup):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    log("decode warmup done")
+
+    # timed region: K whole steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"decode steps timed: {ms_per_step * 1e3:.1f} us/step")
+
+    # the decode kernel alone, bracketed by HIP events on its launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(copies[i % len(copies)], evs[i])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    kv_bytes = int(case.context_lens.astype(np.int64).sum()) * Hkv * 2 * d * 2
+    value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved_gbs = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(kv_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "decode_mfma_kernel<4,16> (paged_attention_decode)",
+                "kernel_avg_us": round(dec_avg_ms * 1e3, 2),
+                "kernel_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                "kernel_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                "algorithmic_bytes_per_launch": kv_bytes}
+    log(f"decode kernel avg {dec_avg_ms * 1e3:.1f} us -> {achieved_gbs:.0f} GB/s")
+    del copies
+    torch.cuda.empty_cache()
+
+    # ----------------------------------------------------------------- prefill
+    prefill = None
+    if not args.no_prefill:
+        t0 = time.perf_counter()
+        pc = wl.make_case(3)
+        log(f"prefill workload generated in {time.perf_counter() - t0:.1f}s: T={pc.total_tokens}")
+        lens = np.diff(pc.cu_seqlens).astype(np.int64)
+        flops = 4.0 * pc.spec.head_dim * pc.spec.num_q_heads * float((lens * (lens + 1) // 2).sum())
+        pq, pk, pv, pcu = up(pc.q), up(pc.k), up(pc.v), up(pc.cu_seqlens)
+        pout = torch.empty_like(pq)
+        plse = torch.empty((pc.total_tokens, pc.spec.num_q_heads), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ops.varlen_causal_prefill(pq, pk, pv, pcu, pc.max_seqlen, pc.scale, out=pout, lse=plse)
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.prefill_iters)]
+        for a, b in pev:
+            a.record(stream)
+            ops.varlen_causal_prefill(pq, pk, pv, pcu, pc.max_seqlen, pc.scale, out=pout, lse=plse)
+            b.record(stream)
+        torch.cuda.synchronize()
+        pms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+        tflops = flops / (pms * 1e-3) / 1e12
+        # paged write-through of the prompt K/V
+        pool = torch.empty((pc.num_blocks, pc.spec.num_kv_heads, pc.spec.block_size, pc.spec.head_dim),
+                           dtype=torch.bfloat16, device=dev)
+        pool_v = torch.empty_like(pool)
+        slots = up(pc.slot_mapping)
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in wev:
+            a.record(stream)
+            ops.paged_kv_write(pk, pv, pool, pool_v, slots)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wms = float(np.mean([a.elapsed_time(b) for a, b in wev]))
+        wbytes = 2 * 2 * pc.total_tokens * pc.spec.num_kv_heads * pc.spec.head_dim * 2  # read + write, K and V
+        prefill = {"workload": pc.spec.name, "total_tokens": pc.total_tokens,
+                   "kernel_avg_us": round(pms * 1e3, 1), "tflops": round(tflops, 1),
+                   "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                                "traffic": None, "algorithmic_flops_per_launch": flops},
+                   "kv_write": {"kernel_avg_us": round(wms * 1e3, 1),
+                                "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)}}
+        log(f"prefill {pms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; prompt kv write {wms * 1e3:.1f} us")
+        del pq, pk, pv, pout, pool, pool_v
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover - threadpoolctl is optional
+            blas_threads = 1
+        t0 = time.perf_counter()
+        kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
+        n_done = 0
+        bytes_done = 0
+        for b in range(B):  # whole sequences until ~10 s of CPU work
+            oracle.decode(case.q[b:b + 1], kc, vc, case.block_tables[b:b + 1], case.context_lens[b:b + 1],
+                          bs, case.scale, spec.dtype)
+            n_done += 1
+            bytes_done += int(case.context_lens[b]) * Hkv * 2 * d * 2
+            if time.perf_counter() - t0 > 10.0:
+                break
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(bytes_done / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+               "kind": "oracle",
+               "sample": f"fp64 NumPy oracle: paged write of the 64 new tokens + decode of the first "
+                         f"{n_done} of 64 sequences of the same workload ({bytes_done / 1e6:.1f} MB of KV) "
+                         f"in {cpu_s:.2f} s; host cpu_count={os.cpu_count()} "
+                         f"affinity={len(os.sched_getaffinity(0))}"}
+        log(f"cpu baseline {cpu['value']} GB/s on {n_done} sequences")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "block_size": bs, "context_lens": "uniform[128,2048], seed 1002",
+                   "sum_context": int(case.context_lens.sum()), "num_blocks": case.num_blocks,
+                   "partition_size": ps, "input_copies": len(range(max(1, args.copies))),
+                   "step": "paged_kv_write(64 tokens) + paged_attention_decode + paged_attention_reduce",
+                   "kv_bytes_per_step": kv_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

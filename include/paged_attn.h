@@ -1,0 +1,195 @@
+/*
+ * paged_attn.h - C ABI of the MI355X (gfx950) attention-over-paged-KV library.
+ *
+ * Four calls make up the hot path of attention over a paged KV cache:
+ *   paged_kv_write          scatter new K/V rows into fixed-size physical blocks
+ *   paged_attention_decode  one query token per sequence against its paged history
+ *   paged_attention_reduce  log-sum-exp merge of split-KV partitions
+ *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *   library allocates and frees nothing, never synchronises, and never reads
+ *   device memory from the host.  Every call is asynchronous on `stream` (a
+ *   hipStream_t; NULL means the default stream) and returns as soon as its
+ *   kernels are enqueued.
+ * Layouts (all row-major, densely packed, no strides):
+ *   KV pool           k_cache, v_cache : [num_blocks, num_kv_heads, block_size, head_dim]
+ *                     one contiguous block_size x head_dim slab per (block, KV head)
+ *   block_tables      int32 [num_seqs, max_blocks_per_seq]; entry j is the physical
+ *                     block holding positions j*block_size .. (j+1)*block_size-1;
+ *                     unused entries hold -1
+ *   context_lens      int32 [num_seqs]; the number of cached positions a sequence's
+ *                     query attends to, the position just written included
+ *   slot_mapping      int32 [num_tokens]; slot = block * block_size + offset; < 0 skips
+ *   cu_seqlens        int32 [num_seqs + 1]; cu_seqlens[0] = 0, non-decreasing
+ * Element types.  PA_F32 = IEEE float32; PA_BF16 = bfloat16 (raw 16-bit patterns).
+ *   q / k / v / out / caches use the call's dtype; lse and partial results are
+ *   always float32.  Outputs in bf16 are rounded to nearest-even from float32.
+ * GQA.  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Softmax statistics.  lse = natural log of the sum of exp(scale * q.k) over the
+ *   keys a query sees; a query that sees no key gets out = 0 and lse = -inf.
+ * Device-resident contents are preconditions the host cannot check without a
+ *   sync: block ids in [0, num_blocks), unique slots below num_blocks*block_size,
+ *   context_lens <= max_context_len, cu_seqlens within [0, total_tokens].  The
+ *   kernels never access memory outside the buffers whatever these hold: a slot
+ *   or block id out of range is skipped, a context length is clamped, and the
+ *   result for such inputs is unspecified (but finite-time and fault-free).
+ * Errors.  Each call returns PA_OK (0) or a PA_ERR_* code and then leaves a
+ *   message for pa_last_error().  Host-side validation happens before any
+ *   launch, so an error return means nothing was enqueued (PA_ERR_LAUNCH aside).
+ *   Nothing throws or aborts across the ABI.
+ *
+ * Sources for the operations: the pages "Llama 4 inference doubling
+ * (FlashAttention-3 + PagedAttention + vLLM)" (section 2.4: varlen call with
+ * cu_seqlens, causal, returning out and lse; section 3.1: logical pages mapped
+ * to physical blocks through an int32 table, -1 = unallocated; section 3.2:
+ * 16-token blocks, power of two), "LLM inference optimisation: KV cache to
+ * FlashAttention" (section 3.1: block table lookup then in-place update of
+ * preallocated KV blocks), "PageAttention + FlashAttention golden combination"
+ * (section 2.1: fixed-size blocks anywhere in memory, shared prompt blocks) and
+ * "LLaMA inference performance: structure and source" (section 2.1: GQA groups;
+ * section 3.1: scores, mask, softmax, weighted sum).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent arguments */
+  PA_ERR_UNSUPPORTED = 2, /* valid but no kernel for this dtype/head_dim/block_size */
+  PA_ERR_LAUNCH = 3       /* the HIP runtime rejected a launch */
+};
+
+/* Version of this ABI (bumped on any signature or semantic change). */
+int pa_abi_version(void);
+
+/* Process-wide options.  PA_OPT_FORCE_VECTOR_PATH (value 0/1): run decode and
+ * prefill on their vector-ALU kernels even where an MFMA kernel exists (both
+ * compute the same result; used to cross-check one kernel against the other).
+ * Returns PA_OK or PA_ERR_INVALID_ARG for an unknown option.  Not thread-safe
+ * against concurrent calls. */
+enum { PA_OPT_FORCE_VECTOR_PATH = 1 };
+int pa_set_option(int option, int value);
+
+/* Message describing the last error returned on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on that thread. */
+const char* pa_last_error(void);
+
+/*
+ * paged_kv_write - write new tokens' K and V rows into the paged pools.
+ *
+ * For each t < num_tokens with s = slot_mapping[t] >= 0, and every KV head h:
+ *   k_cache[s / block_size, h, s % block_size, :] = k[t, h, :]
+ *   v_cache[s / block_size, h, s % block_size, :] = v[t, h, :]
+ * A bit-exact copy; every other byte of the pools is left untouched.  This is
+ * the in-place update through the block table that replaces re-allocating a
+ * contiguous cache on every appended token.
+ *   k, v          [num_tokens, num_kv_heads, head_dim], dtype
+ *   k_cache, v_cache  pools as above, dtype; updated in place
+ *   slot_mapping  int32 [num_tokens]; slots must be unique; s < 0 skips token t;
+ *                 s >= num_blocks * block_size is skipped (precondition violation)
+ * num_tokens = 0 is a no-op.  Supported: head_dim * sizeof(dtype) a multiple of 16.
+ */
+int paged_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                   const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                   int head_dim, int block_size, int num_blocks, pa_dtype dtype,
+                   void* stream);
+
+/*
+ * paged_attention_decode - attention of one query token per sequence over its
+ * paged history (PagedAttention decode), with GQA and online softmax.
+ *
+ * For sequence b and query head h (KV head g = h / G), over positions
+ * p < ctx = context_lens[b], each fetched from block block_tables[b][p / block_size]
+ * at offset p % block_size:
+ *   out[b, h, :] = sum_p softmax_p(scale * q[b,h,:] . K[p,g,:]) V[p,g,:]
+ *   lse[b, h]    = log sum_p exp(scale * q[b,h,:] . K[p,g,:])
+ * partition_size == 0: one pass per (sequence, KV head); writes out ([B, H_q, d],
+ *   dtype) and lse ([B, H_q], float32).  part_out/part_lse are not touched.
+ * partition_size > 0 (split-KV): positions are cut into partitions
+ *   [i*partition_size, (i+1)*partition_size); for every partition i that holds at
+ *   least one position (i*partition_size < ctx) the call writes the attention over
+ *   that partition alone to part_out[b, h, i, :] (float32) and part_lse[b, h, i]
+ *   (float32).  Partitions past the end are not written.  out/lse are not touched;
+ *   paged_attention_reduce merges the partitions.  partition_size must be a
+ *   multiple of block_size.  The partition dimension of part_out/part_lse is
+ *   max_partitions = ceil(max_context_len / partition_size).
+ *   q             [B, H_q, head_dim], dtype
+ *   block_tables  int32 [B, max_blocks_per_seq]
+ *   context_lens  int32 [B]; each <= max_context_len
+ *   max_context_len  host-side upper bound on context_lens (sizes the grid);
+ *                 must be <= max_blocks_per_seq * block_size
+ *   scale         multiplies q.k (typically 1/sqrt(head_dim))
+ * Supported: dtype f32 or bf16; head_dim 64 or 128; block_size 8, 16, 32 or 64;
+ *   H_q / H_kv in {1, 2, 4, 8}; num_seqs <= 65535.
+ */
+int paged_attention_decode(void* out, float* lse, float* part_out, float* part_lse,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int max_blocks_per_seq, int num_blocks,
+                           int partition_size, int max_context_len, float scale,
+                           pa_dtype dtype, void* stream);
+
+/*
+ * paged_attention_reduce - merge split-KV partitions by log-sum-exp.
+ *
+ * For sequence b, head h, the live partitions are i < n = ceil(ctx / partition_size)
+ * (ctx = context_lens[b], n capped at max_partitions).  With M = max_i part_lse[b,h,i]
+ * and w_i = exp(part_lse[b,h,i] - M):
+ *   out[b, h, :] = sum_i w_i part_out[b,h,i,:] / sum_i w_i     (dtype)
+ *   lse[b, h]    = M + log(sum_i w_i)                          (float32)
+ * Partitions at or past n are never read; a sequence with ctx = 0 gets out = 0 and
+ * lse = -inf.  part_out [B, H_q, max_partitions, head_dim] and
+ * part_lse [B, H_q, max_partitions] are float32, as written by
+ * paged_attention_decode with the same partition_size.
+ */
+int paged_attention_reduce(void* out, float* lse, const float* part_out,
+                           const float* part_lse, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int head_dim,
+                           int partition_size, int max_partitions, pa_dtype dtype,
+                           void* stream);
+
+/*
+ * varlen_causal_prefill - causal self-attention of sequences packed back to back.
+ *
+ * Sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of q, k and v.  Row i
+ * of sequence s (token t = cu_seqlens[s] + i) and query head h attend to the keys
+ * of tokens cu_seqlens[s] .. t (same sequence, causal, the token itself included)
+ * of KV head h / G:
+ *   out[t, h, :] = sum_j softmax_j(scale * q[t,h,:] . k[j,g,:]) v[j,g,:]
+ *   lse[t, h]    = log sum_j exp(scale * q[t,h,:] . k[j,g,:])
+ *   q, out        [total_tokens, H_q, head_dim], dtype
+ *   k, v          [total_tokens, H_kv, head_dim], dtype
+ *   lse           float32 [total_tokens, H_q]
+ *   cu_seqlens    int32 [num_seqs + 1]
+ *   max_seqlen    host-side upper bound on any sequence length (sizes the grid);
+ *                 rows of a longer sequence beyond max_seqlen are not computed
+ * Tokens not covered by any sequence are not written.  The K/V are read from the
+ * packed arrays, not from a paged pool; writing them into a pool is a separate
+ * paged_kv_write call.
+ * Supported: dtype bf16, head_dim 128 (MFMA path); dtype f32 or bf16 with
+ *   head_dim 64 or 128 (vector path); H_q / H_kv in {1, 2, 4, 8}; num_seqs <= 65535.
+ *   max_seqlen must not exceed total_tokens.
+ */
+int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k,
+                          const void* v, const int32_t* cu_seqlens, int num_seqs,
+                          int total_tokens, int max_seqlen, int num_q_heads,
+                          int num_kv_heads, int head_dim, float scale, pa_dtype dtype,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -144,8 +144,9 @@ def decode_one(q, k_cache, v_cache, block_tables, context_lens, block_size,
     Hkv = k_cache.shape[1]
     ctx = int(context_lens[b])
     g = group_of(h, Hq, Hkv)
-    K = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)[:, g, :]
-    V = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)[:, g, :]
+    # gather from the KV head's slice of the pool only (a view, same bytes)
+    K = upcast(gather(k_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype)[:, 0, :]
+    V = upcast(gather(v_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype)[:, 0, :]
     if positions is not None:
         lo, hi = positions
         K, V = K[lo:hi], V[lo:hi]

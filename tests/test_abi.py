@@ -1,0 +1,117 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its host-side
+validation rejects bad arguments before any launch.  No GPU needed: every call
+here returns from validation without touching the HIP runtime's devices."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_paged_kv_write_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from attention_paged_kv_write_amd import build
+        build.build()
+    return ops.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("paged_kv_write", "paged_attention_decode", "paged_attention_reduce",
+              "varlen_causal_prefill"):
+        assert n in names
+    assert set(names) == set(ops.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version(lib):
+    assert lib.pa_abi_version() == 1
+
+
+def _decode(lib, **kw):
+    a = dict(B=2, Hq=8, Hkv=2, d=128, bs=16, mbps=4, NB=10, psize=0, maxctx=64, scale=0.1, dt=1)
+    a.update(kw)
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails or num_seqs == 0
+    return lib.paged_attention_decode(p, p, p, p, p, p, p, p, p, a["B"], a["Hq"], a["Hkv"], a["d"],
+                                      a["bs"], a["mbps"], a["NB"], a["psize"], a["maxctx"],
+                                      a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), 1),            # H_q % H_kv != 0
+    (dict(Hkv=0), 1),
+    (dict(maxctx=65), 1),              # > max_blocks_per_seq * block_size
+    (dict(psize=24), 1),               # not a multiple of block_size
+    (dict(psize=-16), 1),
+    (dict(dt=7), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(B=-1), 1),
+    (dict(d=96), 2),                   # unsupported head_dim
+    (dict(bs=12, maxctx=48), 2),       # unsupported block_size
+    (dict(Hq=48, Hkv=2), 2),           # GQA group 24
+    (dict(B=70000), 2),
+    (dict(B=0), 0),                    # nothing to do
+])
+def test_decode_validation(lib, kw, code):
+    assert _decode(lib, **kw) == code
+    if code:
+        assert lib.pa_last_error().decode().startswith("paged_attention_decode")
+
+
+def test_decode_null_pointers(lib):
+    rc = lib.paged_attention_decode(None, None, None, None, None, None, None, None, None,
+                                    2, 8, 2, 128, 16, 4, 10, 0, 64, 0.1, 1, None)
+    assert rc == 1 and "null" in lib.pa_last_error().decode()
+
+
+def test_write_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.paged_kv_write(p, p, p, p, p, -1, 8, 128, 16, 10, 1, None) == 1
+    assert lib.paged_kv_write(p, p, p, p, p, 4, 8, 128, 16, 0, 1, None) == 1
+    assert lib.paged_kv_write(p, p, p, p, p, 4, 8, 4, 16, 10, 1, None) == 2  # 8 bytes per row
+    assert lib.paged_kv_write(None, None, None, None, None, 4, 8, 128, 16, 10, 1, None) == 1
+    assert lib.paged_kv_write(p, p, p, p, p, 4, 8, 128, 1 << 20, 1 << 12, 1, None) == 1  # slots > int32
+    assert lib.paged_kv_write(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == 0
+
+
+def test_reduce_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.paged_attention_reduce(p, p, p, p, p, 2, 8, 128, 0, 4, 1, None) == 1
+    assert lib.paged_attention_reduce(p, p, p, p, p, 2, 8, 128, 512, 0, 1, None) == 1
+    assert lib.paged_attention_reduce(p, p, p, p, p, 2, 8, 80, 512, 4, 1, None) == 2
+    assert lib.paged_attention_reduce(None, None, None, None, None, 2, 8, 128, 512, 4, 1, None) == 1
+    assert lib.paged_attention_reduce(p, p, p, p, p, 0, 8, 128, 512, 4, 1, None) == 0
+
+
+def test_prefill_validation(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.varlen_causal_prefill
+    assert f(p, p, p, p, p, p, 2, 100, 60, 32, 6, 128, 0.1, 1, None) == 1     # 32 % 6
+    assert f(p, p, p, p, p, p, 2, 100, 101, 32, 8, 128, 0.1, 1, None) == 1    # max_seqlen > T
+    assert f(p, p, p, p, p, p, 2, 100, 60, 32, 8, 72, 0.1, 1, None) == 2      # head_dim
+    assert f(None, None, None, None, None, None, 2, 100, 60, 32, 8, 128, 0.1, 1, None) == 1
+    assert f(p, p, p, p, p, p, 0, 100, 60, 32, 8, 128, 0.1, 1, None) == 0
+
+
+def test_option(lib):
+    assert lib.pa_set_option(99, 1) == 1
+    assert lib.pa_set_option(ops.PA_OPT_FORCE_VECTOR_PATH, 0) == 0

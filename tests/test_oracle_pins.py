@@ -474,3 +474,28 @@ def test_generator_layout(cfg, over):
             used[blk, p % bs] = True
             assert np.isfinite(kf[blk, :, p % bs]).all()
     assert np.isnan(kf.transpose(0, 2, 1, 3)[~used]).all()
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (1, {}),
+    (2, dict(batch=8, ctx_min=100, ctx_max=700, max_blocks_per_seq=44)),
+    (4, dict(batch=8, ctx_min=600, ctx_max=900, max_blocks_per_seq=29)),
+])
+def test_needle_on_workloads(cfg, over):
+    """The needle inputs the GPU tests use select exactly one value row in the oracle."""
+    from tests.gpu_util import needle_case, needle_targets, storage_to_f64
+    rng = np.random.default_rng(77)
+    for r in (0, 5, 63):
+        case = wl.make_case(cfg, **over)
+        targets = needle_targets(case, r, rng)
+        case = needle_case(case, targets)
+        bs = case.spec.block_size
+        kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
+        out, lse = oracle.decode(case.q, kc, vc, case.block_tables, case.context_lens, bs, case.scale,
+                                 case.spec.dtype)
+        G = case.spec.num_q_heads // case.spec.num_kv_heads
+        for b, t in enumerate(targets):
+            v = storage_to_f64(vc[case.block_tables[b, t // bs], :, t % bs, :])
+            for h in range(case.spec.num_q_heads):
+                np.testing.assert_allclose(out[b, h], v[h // G], rtol=1e-60, atol=0)
+            assert np.all(np.abs(lse[b] - 200.0) < 2.0)

@@ -1,0 +1,123 @@
+"""GPU parity of varlen_causal_prefill against the fp64 CPU oracle, through the C ABI.
+
+Shrunk workloads are compared on every output; the full Llama-3-8B varlen
+workload (16 sequences, about 16.9k tokens) on a sample of heads.  Row 0 of
+each sequence must return v_0 bit-exactly (this pins the cu_seqlens
+boundaries), and the last row of each sequence must match a decode over a
+paged pool written from the same K/V (cross-path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_paged_kv_write_amd import ops
+from attention_paged_kv_write_amd import workloads as wl
+from tests.gpu_util import assert_parity, to_dev, to_host_bits, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(case):
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    cu = to_dev(case.cu_seqlens)
+    out, lse = ops.varlen_causal_prefill(q, k, v, cu, case.max_seqlen, case.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+PREFILL_CASES = {
+    "ragged_small": dict(num_seqs=6, lens_fixed=(1, 63, 64, 65, 130, 300)),
+    "single_seq": dict(num_seqs=1, lens_fixed=(257,)),
+    "g8": dict(num_seqs=3, lens_fixed=(5, 100, 200), num_q_heads=16, num_kv_heads=2),
+    "g1": dict(num_seqs=3, lens_fixed=(17, 64, 129), num_q_heads=4, num_kv_heads=4),
+    "f32_d64": dict(dtype=wl.F32, num_seqs=4, lens_fixed=(1, 10, 33, 70), num_q_heads=4,
+                    num_kv_heads=2, head_dim=64),
+    "bf16_d64": dict(num_seqs=3, lens_fixed=(3, 40, 90), num_q_heads=4, num_kv_heads=2, head_dim=64),
+    "f32_d128": dict(dtype=wl.F32, num_seqs=2, lens_fixed=(31, 77), num_q_heads=8, num_kv_heads=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_prefill_matches_oracle(name):
+    case = wl.make_case(3, **PREFILL_CASES[name])
+    out, lse = run_prefill(case)
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["ragged_small", "g8"])
+def test_prefill_vector_kernel_matches_oracle(name):
+    case = wl.make_case(3, **PREFILL_CASES[name])
+    try:
+        ops.set_force_vector_path(True)
+        out, lse = run_prefill(case)
+    finally:
+        ops.set_force_vector_path(False)
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, name + " vector")
+
+
+def test_prefill_row0_is_v0_bit_exact():
+    case = wl.make_case(3, **PREFILL_CASES["ragged_small"])
+    out, lse = run_prefill(case)
+    ob = to_host_bits(out)
+    lh = to_host_f64(lse)
+    G = case.spec.num_q_heads // case.spec.num_kv_heads
+    for s in range(case.spec.num_seqs):
+        a = int(case.cu_seqlens[s])
+        for h in range(case.spec.num_q_heads):
+            assert ob[a, h].tobytes() == case.v[a, h // G].tobytes(), (s, h)
+            _, l1, _ = oracle.attend(oracle.upcast(case.q[a, h], wl.BF16),
+                                     oracle.upcast(case.k[a:a + 1, h // G], wl.BF16),
+                                     oracle.upcast(case.v[a:a + 1, h // G], wl.BF16), case.scale)
+            assert abs(lh[a, h] - l1) <= 1e-3
+
+
+def test_prefill_leaves_uncovered_tokens_untouched():
+    # cu_seqlens covering only part of the buffer: tokens outside are not written
+    case = wl.make_case(3, **PREFILL_CASES["ragged_small"])
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    T = q.shape[0]
+    cu = to_dev(np.array([0, 64, 129], np.int32))  # first two sequences only
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((T, q.shape[1]), 7.0, device=q.device)
+    ops.varlen_causal_prefill(q, k, v, cu, 65, case.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out[129:] == 7.0) and torch.all(lse[129:] == 7.0)
+    ref_out, ref_lse = oracle.prefill(case.q[:129], case.k[:129], case.v[:129],
+                                      np.array([0, 64, 129]), case.scale, wl.BF16)
+    assert_parity(to_host_f64(out[:129]), to_host_f64(lse[:129]), ref_out, ref_lse, wl.BF16, "partial")
+
+
+def test_prefill_write_then_decode_cross_path():
+    case = wl.make_case(3, num_seqs=4, lens_fixed=(1, 50, 128, 333))
+    spec = case.spec
+    out, lse = run_prefill(case)
+    pk = wl.empty_pool(case.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim, spec.dtype)
+    kc, vc = to_dev(pk), to_dev(pk.copy())
+    ops.paged_kv_write(to_dev(case.k), to_dev(case.v), kc, vc, to_dev(case.slot_mapping))
+    last = case.cu_seqlens[1:] - 1
+    lens = np.diff(case.cu_seqlens).astype(np.int32)
+    dout, dlse = ops.paged_attention_decode(to_dev(case.q[last]), kc, vc, to_dev(case.block_tables),
+                                            to_dev(lens), int(lens.max()), case.scale)
+    torch.cuda.synchronize()
+    # the decode and the prefill agree with the oracle's decode of the same rows
+    ek, ev = oracle.kv_write(pk, pk.copy(), case.k, case.v, case.slot_mapping, spec.block_size)
+    ref_out, ref_lse = oracle.decode(case.q[last], ek, ev, case.block_tables, lens, spec.block_size,
+                                     case.scale, spec.dtype)
+    assert_parity(to_host_f64(dout), to_host_f64(dlse), ref_out, ref_lse, spec.dtype, "decode of prompt")
+    assert_parity(to_host_f64(out)[last], to_host_f64(lse)[last], ref_out, ref_lse, spec.dtype,
+                  "prefill last rows")
+
+
+@pytest.mark.slow
+def test_prefill_full_size_sampled_heads():
+    case = wl.make_case(3)
+    out, lse = run_prefill(case)
+    oh, lh = to_host_f64(out), to_host_f64(lse)
+    heads = [0, 13, 31]
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, wl.BF16,
+                                      heads=heads)
+    assert_parity(oh[:, heads], lh[:, heads], ref_out[:, heads], ref_lse[:, heads], wl.BF16, "full C3")
+    assert np.isfinite(oh).all() and np.isfinite(lh).all()
