@@ -36,7 +36,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 DECODE_SOURCES = ("attention_paged_kv_write_amd/csrc/decode.hip",
                   "attention_paged_kv_write_amd/csrc/common.h",
                   "attention_paged_kv_write_amd/csrc/kernels.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.txt")
 
 
 def log(msg):
@@ -74,6 +74,9 @@ def main(argv=None):
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -92,6 +95,17 @@ def main(argv=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                          "bytes_written_per_copy": n, "copies": 5}))
+        return
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -231,19 +245,19 @@ def main(argv=None):
         kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
         n_done = 0
         bytes_done = 0
-        for b in range(B):  # whole sequences until ~10 s of CPU work
+        while time.perf_counter() - t0 < args.cpu_seconds:  # whole sequences, ~10 s of CPU work
+            b = n_done % B
             oracle.decode(case.q[b:b + 1], kc, vc, case.block_tables[b:b + 1], case.context_lens[b:b + 1],
                           bs, case.scale, spec.dtype)
             n_done += 1
             bytes_done += int(case.context_lens[b]) * Hkv * 2 * d * 2
-            if time.perf_counter() - t0 > 10.0:
-                break
         cpu_s = time.perf_counter() - t0
         cpu = {"value": round(bytes_done / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
                "kind": "oracle",
-               "sample": f"fp64 NumPy oracle: paged write of the 64 new tokens + decode of the first "
-                         f"{n_done} of 64 sequences of the same workload ({bytes_done / 1e6:.1f} MB of KV) "
-                         f"in {cpu_s:.2f} s; host cpu_count={os.cpu_count()} "
+               "sample": f"fp64 NumPy oracle on the same workload: paged write of the 64 new tokens, "
+                         f"then decode of {n_done} sequences in order, cycling over the 64 "
+                         f"({n_done / B:.1f} passes, {bytes_done / 1e6:.1f} MB of KV) in {cpu_s:.2f} s; "
+                         f"BLAS threads {blas_threads}, host cpu_count={os.cpu_count()} "
                          f"affinity={len(os.sched_getaffinity(0))}"}
         log(f"cpu baseline {cpu['value']} GB/s on {n_done} sequences")
 
