@@ -119,6 +119,7 @@ int paged_attention_decode(void* out, float* lse, float* part_out, float* part_l
   if (partition_size > 0) {
     if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
     num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
   } else if (!out || !lse) {
     return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
   }

@@ -102,4 +102,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// 16 bytes per lane straight from global memory into LDS (no VGPRs): lane l's
+// bytes land at lds_base + 16*l; lds_base must be wave-uniform.  Completion is
+// counted by vmcnt.  (A plain device function: called inside a lambda, the
+// builtin would also be instantiated for the host, where it does not exist.)
+__device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  typedef __attribute__((address_space(1))) void* gbl_ptr;
+  __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)lds_base, 16, 0, 0);
+}
+
+// 32-bit LDS byte address of a __shared__ object (for inline-asm DS operands).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const void* lds_cptr;
+  return static_cast<uint32_t>((uintptr_t)((lds_cptr)p));
+}
+
 }  // namespace pa

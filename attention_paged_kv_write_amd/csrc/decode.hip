@@ -67,7 +67,7 @@ __device__ __forceinline__ Range work_range(const DecodeArgs& a, int b, int part
 
 // Final cross-wave merge of (m, l, acc) held in LDS and the store of the result.
 // sm_m/sm_l: [4][G]; sm_acc: [4][G][D].  m is in log2 units.
-template <bool BF, int D, int G>
+template <bool BF, int D, int G, int W = 4>
 __device__ __forceinline__ void merge_and_store(const DecodeArgs& a, int b, int g, int part,
                                                 const float (*sm_m)[G], const float (*sm_l)[G],
                                                 const float (*sm_acc)[G][D]) {
@@ -76,12 +76,12 @@ __device__ __forceinline__ void merge_and_store(const DecodeArgs& a, int b, int 
     const int e = idx - h * D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
     float o = 0.f, lse = kNegInf;
     if (M != kNegInf) {
       float L = 0.f, acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float f = fast_exp2(sm_m[w][h] - M);
         L += f * sm_l[w][h];
         acc += f * sm_acc[w][h][e];
@@ -140,13 +140,14 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   __shared__ float sm_l[4][G];
   __shared__ float sm_acc[4][G][D];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
   const Range r = work_range(a, b, part);
   if (r.blk_lo >= r.blk_hi) {
     if (a.partition_size == 0) store_empty<BF, D, G>(a, b, g);
     return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int rg = lane / LPT, dl = lane % LPT;
   const int BS = a.block_size;
 
@@ -258,32 +259,91 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   merge_and_store<BF, D, G>(a, b, g, part, sm_m, sm_l, sm_acc);
 }
 
+// Read one decode tile back from its LDS slot: wait until at most VMCNT
+// LDS-DMA loads (those of the newer slots) are still in flight, issue the four
+// lane-linear 16-byte K reads and the eight transposed V reads, and wait for
+// them.  Written as one asm block because the compiler cannot count LDS-DMA
+// completions across the ring and would otherwise drain every load in flight.
+// The asm exists only in the device pass (its register constraints are
+// meaningless to the host compiler).
+template <int VMCNT>
+__device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const uint32_t* k_addr,
+                                                     const uint32_t* v_addr, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "s_waitcnt vmcnt(%24)\n\t"
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(kw[2]), "=&v"(kw[3]), "=&v"(vt[0]), "=&v"(vt[1]),
+        "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]), "=&v"(vt[6]), "=&v"(vt[7])
+      : "v"(k_addr[0] + off), "v"(k_addr[1] + off), "v"(k_addr[2] + off), "v"(k_addr[3] + off),
+        "v"(v_addr[0] + off), "v"(v_addr[1] + off), "v"(v_addr[2] + off), "v"(v_addr[3] + off),
+        "v"(v_addr[4] + off), "v"(v_addr[5] + off), "v"(v_addr[6] + off), "v"(v_addr[7] + off),
+        "i"(VMCNT)
+      : "memory");
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel: bf16, head_dim 128, block_size a multiple of 16
 // ---------------------------------------------------------------------------
-template <int G, int BS>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+// W waves per workgroup: W = 1 in split-KV mode (one wave owns one partition,
+// so every work unit of a launch can be resident at once and no cross-wave
+// merge is needed); W = 4 for the single-pass mode (the waves take the
+// sequence's blocks round-robin and meet in LDS).
+//
+// Per 16-token tile of KV head g:
+//   S^T[16 tok x 16 col] = K[16 x 128] . Q^T   four v_mfma_f32_16x16x32_bf16; K
+//       comes straight from HBM into the A operand (lane (j, c16): token c16,
+//       dims 32c + 8j), the group's query heads are the B operand columns.
+//   online softmax on S^T: lane (j, c16) holds tokens 4j..4j+3 of column c16,
+//       so the running max/rescale of a column stay in its own lanes; the tile
+//       max needs one exchange across the four 16-lane rows.
+//   O^T[128 d x 16 col] += V^T . P^T   eight v_mfma_f32_16x16x16_bf16: the
+//       S^T accumulator layout is exactly the P^T B operand (4 consecutive
+//       tokens of one column per lane), and V^T comes from LDS through
+//       ds_read_b64_tr_b16, which hands each lane 4 consecutive tokens of one
+//       dim from a row-major V tile.
+// V tiles reach LDS by global_load_lds_dwordx4 (no VGPRs), three slots per
+// wave, so two tiles are in flight while one is computed.  Lane l of load k
+// fetches 16 bytes of token 4k + l/16, chunk (l%16) ^ 2*(token%8): the XOR
+// spreads the eight tokens a transposed read touches over all 64 banks.
+template <int G, int BS, int W, int NS>
+__global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int RC = D * 2 / 16;   // 16-byte chunks per row (16)
   constexpr int TPB = BS / 16;     // 16-token tiles per block
+  typedef short short4v __attribute__((ext_vector_type(4)));
 
-  __shared__ float sm_p[4][16][G];
-  __shared__ float sm_alpha[4][G];
-  __shared__ float sm_m[4][G];
-  __shared__ float sm_l[4][G];
-  __shared__ float sm_acc[4][G][D];
+  // LDS ring, per slot and wave: K tile (4 KB, MFMA A layout, lane-linear)
+  // then V tile (4 KB, row-major, chunk-swizzled)
+  constexpr int kSlotBytes = 512 * 16;
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][512];
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  __shared__ float sm_acc[W > 1 ? W : 1][G][D];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const Range r = work_range(a, b, part);
-  if (r.blk_lo >= r.blk_hi) {
-    if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
-    return;
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
+  const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  const int blk_lo = a.partition_size > 0 ? part * (a.partition_size / BS) : 0;
 
-  // The group's query heads as the MFMA B operand: lane (j, c16) holds
-  // q[head c16][8 dims starting at 32c + 8j] for c = 0..3; padding columns 0.
+  // First round trip: context length, the group's queries, and the first
+  // window of block ids (speculative: bounded by the table row, masked below).
+  const int ctx_raw = a.context_lens[b];
   bf16x8 qf[4];
   {
     const u32x4* qc = static_cast<const u32x4*>(a.q);
@@ -295,130 +355,200 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       qf[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  auto load_ids = [&](int w0) -> int {
+    const int e = blk_lo + wave + W * (w0 + lane);
+    return e < a.max_blocks_per_seq ? table[e] : -1;
+  };
+  int ids = load_ids(0);
 
-  float m = kNegInf;   // running max (log2 units) of head column c16
-  float l = 0.f;       // this lane's share of the running sum
-  float acc[G][8];     // P.V: rows j + 4k of each tile, dims 8*c16 .. 8*c16+7
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
+  const Range r = work_range(a, b, part);
+  (void)ctx_raw;
+  if (r.blk_lo >= r.blk_hi) {
+    if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
+    return;
+  }
   const int span = r.blk_hi - r.blk_lo;
-  const int n_tiles = (span > wave ? (span - wave + 3) >> 2 : 0) * TPB;
+  const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;
+
+  float m = kNegInf;   // running max (log2 units) of column c16
+  float l = 0.f;       // this lane's share of the running sum of column c16
+  floatx4 oacc[8];     // O^T: dims 16dn + 4j + i of column c16
+#pragma unroll
+  for (int dn = 0; dn < 8; ++dn) oacc[dn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
   const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
   const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
-  const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
 
-  // Issue the loads of tile n: K in MFMA A layout (token c16, dims 32c + 8j),
-  // V as plain rows (token j + 4k, dims 8*c16).
-  auto fetch = [&](int n, u32x4* kd, u32x4* vd, int& pos0) -> bool {
-    const int blk = r.blk_lo + wave + 4 * (n / TPB);
-    const int tile = n % TPB;
-    pos0 = blk * BS + tile * 16;
-    const int phys = table[blk];
-    if (phys < 0 || phys >= a.num_blocks) return false;
-    const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + tile * 16) * RC;
+  // transposed-read address pieces (constant per lane): token 4j + c16/4,
+  // dims 16dn + 4(c16%4) .. +3
+  // (the chunk of dims 16dn + 4(c16%4) is 2dn + tr_half, stored at
+  // (2dn + tr_half) ^ 2*(tok%8) = 2*(dn ^ tr_t8) + tr_half)
+  const int tr_tok = 4 * j + (c16 >> 2);
+  const int tr_t8 = tr_tok & 7;
+  const int tr_half = (c16 & 3) >> 1;   // which 8-dim chunk of the 16-dim group
+  const int tr_off = 8 * (c16 & 1);     // byte offset inside the 16-byte chunk
+  // slot-0 LDS addresses of this lane's reads (other slots: + slot * kSlotBytes)
+  // K row t, dim chunk q is stored at chunk q ^ t of the slot's row t; the MFMA
+  // A operand of instruction c wants row c16, chunk 4c + j
+  uint32_t k_addr[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kd[c] = kc[base + c16 * RC + 4 * c + j];
+  for (int c = 0; c < 4; ++c) k_addr[c] = lds_addr(&ring[wave][0][16 * c16 + ((4 * c + j) ^ c16)]);
+  uint32_t v_addr[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vd[k] = vc[base + (j + 4 * k) * RC + c16];
-    return true;
-  };
+  for (int dn = 0; dn < 8; ++dn)
+    v_addr[dn] = lds_addr(&ring[wave][0][256]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
 
-  u32x4 kb[4], vb[4];
-  int pos_cur = 0;
-  bool ok_cur = n_tiles > 0 ? fetch(0, kb, vb, pos_cur) : false;
-  for (int n = 0; n < n_tiles; ++n) {
-    u32x4 kn[4], vn[4];
-    int pos_next = 0;
-    bool ok_next = false;
-    if (n + 1 < n_tiles) ok_next = fetch(n + 1, kn, vn, pos_next);
+  for (int w0 = 0; w0 < n_blocks; w0 += 64) {
+    if (w0 > 0) ids = load_ids(w0);
+    const int wn = min(64, n_blocks - w0);
+    const int nt = wn * TPB;
+    int p0 = 0, p1 = 0, p2 = 0, l0 = 0, l1 = 0, l2 = 0;
 
-    if (ok_cur && pos_cur < r.ctx) {
+    // Issue the loads of window tile n into an LDS slot: K in MFMA A layout
+    // (lane (j, c16) brings token c16, dims 32c + 8j; read back by the same
+    // lane), V row-major with the XOR chunk swizzle.  A block id outside the
+    // pool (a precondition violation) reads block 0 with every token masked.
+    auto fetch = [&](int n, int slot, int& pos0, int& lim) {
+      const int i = n / TPB;
+      const int tile = n % TPB;
+      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + tile * 16;
+      int phys = __builtin_amdgcn_readlane(ids, i);
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      phys = ok ? phys : 0;
+      lim = ok ? r.ctx : 0;
+      const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + tile * 16) * RC;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tok = 4 * c + j;   // row-major: 16 lanes per 256-byte row
+        global_to_lds16(kc + base + tok * RC + (c16 ^ tok), &ring[wave][slot][64 * c]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int tok = 4 * k + j;
+        const u32x4* src = vc + base + tok * RC + (c16 ^ (2 * (tok & 7)));
+        global_to_lds16(src, &ring[wave][slot][256 + 64 * k]);
+      }
+    };
+
+    auto process = [&](int slot, int pos0, int lim) {
+      const uint32_t off = slot * kSlotBytes;
+      // The slot's tile is read back in one block: wait until only the two
+      // newer slots' 16 LDS-DMA loads may still be in flight, read K (four
+      // lane-linear 16-byte reads) and V^T (eight transposed reads), and wait
+      // for the reads.  The compiler cannot count LDS-DMA completions across
+      // the ring, so it would otherwise drain every load in flight here.
+      u32x4 kw[4];
+      u32x2 vt[8];
+      lds_read_decode_tile<8 * (NS - 1)>(kw, vt, k_addr, v_addr, off);
       floatx4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[c]), qf[c], st, 0, 0, 0);
-      // st[i] = score of token pos_cur + 4j + i for head column c16
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[c]), qf[c], st, 0, 0, 0);
+      // st[i]: score of token pos0 + 4j + i for column c16
       float s[4];
       float mx = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[i] = (pos_cur + 4 * j + i < r.ctx) ? st[i] * a.scale_log2 : kNegInf;
+        s[i] = (pos0 + 4 * j + i < lim) ? st[i] * a.scale_log2 : kNegInf;
         mx = fmaxf(mx, s[i]);
       }
       mx = across_rows(mx, OpMax());
       const float m_new = fmaxf(m, mx);
       const float ms = m_new == kNegInf ? 0.f : m_new;
       const float alpha = fast_exp2(m - ms);
+      m = m_new;
+      short4v pb;
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[i] = fast_exp2(s[i] - ms);
-        ps += s[i];
+        const float p = fast_exp2(s[i] - ms);
+        ps += p;
+        pb[i] = static_cast<short>(f32_to_bf16_bits(p));
       }
       l = l * alpha + ps;
-      m = m_new;
-      if (c16 < G) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm_p[wave][4 * j + i][c16] = s[i];
-        if (j == 0) sm_alpha[wave][c16] = alpha;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int dn = 0; dn < 8; ++dn) oacc[dn] *= alpha;
+      // tokens past the end may hold anything (NaN): their V entries are
+      // zero-selected, since a zero probability times NaN is still NaN
+      const bool tail = pos0 + 16 > lim;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = sm_alpha[wave][h];
+      for (int dn = 0; dn < 8; ++dn) {
+        short4v va = __builtin_bit_cast(short4v, vt[dn]);
+        if (tail) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int tok = j + 4 * k;
-        if (pos_cur + tok < r.ctx) {
-          float vf[8];
-          unpack16<true>(vb[k], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float p = sm_p[wave][tok][h];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-          }
+          for (int k = 0; k < 4; ++k) va[k] = (pos0 + 4 * j + k < lim) ? va[k] : short(0);
         }
+        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dn], 0, 0, 0);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      kb[c] = kn[c];
-      vb[c] = vn[c];
-    }
-    ok_cur = ok_next;
-    pos_cur = pos_next;
-  }
+    };
 
-  // Per-wave totals: l over the four rows; acc over the four token-row groups.
-  l = across_rows(l, OpSum());
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = across_rows(acc[h][e], OpSum());
-  if (j == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][h][c16 * 8 + e] = acc[h][e];
-    if (c16 < G) {
-      sm_m[wave][c16] = m;
-      sm_l[wave][c16] = l;
+    // Three-slot ring, unrolled so each slot is a distinct LDS array.  Fetches
+    // are unconditional (clamped to the last tile, an L2-hot reload) so every
+    // path through the loop has the same loads in flight.
+    if constexpr (NS == 3) {
+      fetch(0, 0, p0, l0);
+      fetch(min(1, nt - 1), 1, p1, l1);
+      for (int n = 0; n < nt; n += 3) {
+        fetch(min(n + 2, nt - 1), 2, p2, l2);
+        process(0, p0, l0);
+        fetch(min(n + 3, nt - 1), 0, p0, l0);
+        if (n + 1 < nt) process(1, p1, l1);
+        fetch(min(n + 4, nt - 1), 1, p1, l1);
+        if (n + 2 < nt) process(2, p2, l2);
+      }
+    } else {
+      fetch(0, 0, p0, l0);
+      for (int n = 0; n < nt; n += 2) {
+        fetch(min(n + 1, nt - 1), 1, p1, l1);
+        process(0, p0, l0);
+        fetch(min(n + 2, nt - 1), 0, p0, l0);
+        if (n + 1 < nt) process(1, p1, l1);
+      }
+      (void)p2;
+      (void)l2;
     }
   }
-  __syncthreads();
-  merge_and_store<true, D, G>(a, b, g, part, sm_m, sm_l, sm_acc);
+  // LDS-DMA writes still in flight (the clamped reloads) must land before the
+  // workgroup's LDS is reused or released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  l = across_rows(l, OpSum());
+  if constexpr (W == 1) {
+    if (c16 >= G) return;
+    const float inv = 1.f / l;
+    const float lse = (m + __log2f(l)) * kLn2;
+    const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
+    if (a.partition_size > 0) {
+      const size_t pr = row * a.num_partitions + part;
+#pragma unroll
+      for (int dn = 0; dn < 8; ++dn)
+        *reinterpret_cast<floatx4*>(a.part_out + pr * D + 16 * dn + 4 * j) = oacc[dn] * inv;
+      if (j == 0) a.part_lse[pr] = lse;
+    } else {
+      uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+      for (int dn = 0; dn < 8; ++dn) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[dn][0] * inv, oacc[dn][1] * inv);
+        w[1] = pack_bf16x2(oacc[dn][2] * inv, oacc[dn][3] * inv);
+        *reinterpret_cast<u32x2*>(out + row * D + 16 * dn + 4 * j) = w;
+      }
+      if (j == 0) a.lse[row] = lse;
+    }
+  } else {
+    if (c16 < G) {
+#pragma unroll
+      for (int dn = 0; dn < 8; ++dn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_acc[wave][c16][16 * dn + 4 * j + i] = oacc[dn][i];
+      if (j == 0) {
+        sm_m[wave][c16] = m;
+        sm_l[wave][c16] = l;
+      }
+    }
+    __syncthreads();
+    merge_and_store<true, D, G, W>(a, b, g, part, sm_m, sm_l, sm_acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -426,15 +556,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
+#ifndef PA_DECODE_SLOTS
+#define PA_DECODE_SLOTS 2
+#endif
+
+template <int G, int BS>
+hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.partition_size > 0)
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, PA_DECODE_SLOTS>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, PA_DECODE_SLOTS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_mfma_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   switch (a.block_size) {
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<G, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<G, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_mfma_kernel<G, 64>), grid, dim3(256), 0, s, a); break;
+    case 16: return launch_mfma_gb<G, 16>(a, grid, s);
+    case 32: return launch_mfma_gb<G, 32>(a, grid, s);
+    case 64: return launch_mfma_gb<G, 64>(a, grid, s);
     default: return hipErrorNotSupported;
   }
-  return hipGetLastError();
 }
 
 template <bool BF, int D>
@@ -453,8 +595,10 @@ hipError_t launch_generic_d(const DecodeArgs& a, int G, dim3 grid, hipStream_t s
 
 hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  const dim3 grid(static_cast<unsigned>(a.num_partitions), static_cast<unsigned>(a.num_kv_heads),
-                  static_cast<unsigned>(a.num_seqs));
+  // partition slowest: every sequence's first partitions (all live) dispatch
+  // before the high partitions that only long sequences have
+  const dim3 grid(static_cast<unsigned>(a.num_kv_heads), static_cast<unsigned>(a.num_seqs),
+                  static_cast<unsigned>(a.num_partitions));
   if (dt == DType::BF16 && head_dim == 128 && a.block_size % 16 == 0) {
     switch (G) {
       case 1: return launch_mfma_g<1>(a, grid, s);
@@ -477,8 +621,10 @@ hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_
 // Exposed for tests of the vector-ALU kernel on shapes the MFMA kernel owns.
 hipError_t launch_decode_generic(const DecodeArgs& a, DType dt, int head_dim, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  const dim3 grid(static_cast<unsigned>(a.num_partitions), static_cast<unsigned>(a.num_kv_heads),
-                  static_cast<unsigned>(a.num_seqs));
+  // partition slowest: every sequence's first partitions (all live) dispatch
+  // before the high partitions that only long sequences have
+  const dim3 grid(static_cast<unsigned>(a.num_kv_heads), static_cast<unsigned>(a.num_seqs),
+                  static_cast<unsigned>(a.num_partitions));
   if (dt == DType::BF16) {
     if (head_dim == 64) return launch_generic_d<true, 64>(a, G, grid, s);
     if (head_dim == 128) return launch_generic_d<true, 128>(a, G, grid, s);
