@@ -6,10 +6,11 @@
 // ("Llama 4 inference doubling (FlashAttention-3 + PagedAttention + vLLM)",
 // section 2.4) is what makes the merge exact.
 //
-// One workgroup per (sequence, query head).  Pass 1 finds M; pass 2 turns a
-// chunk of partition lse values into weights held in LDS; pass 3 streams the
-// partition outputs (each wave takes every fourth partition, each lane a pair
-// of dims, 8 partitions in flight per wave) and the four waves meet in LDS.
+// General kernel: one workgroup per (sequence, query head).  Pass 1 finds M;
+// pass 2 turns a chunk of partition lse values into weights held in LDS; pass
+// 3 streams the partition outputs (each wave takes every fourth partition,
+// each lane a pair of dims, 8 partitions in flight per wave) and the four
+// waves meet in LDS.
 #include "kernels.h"
 
 namespace pa {
@@ -85,9 +86,94 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   if (tid == 0) a.lse[row] = (M != kNegInf) ? M + __log2f(W) * kLn2 : kNegInf;
 }
 
+// Few partitions (at most 32): one wave per (sequence, head) issues every
+// load it needs at once -- lane p reads partition p's lse, and each lane
+// reads its D/64 dims of every live partition -- so the merge costs one
+// memory round trip.  Weights are formed per partition from the lse held by
+// lane p (v_readlane).
+template <bool BF, int D, int MAXP>
+__global__ __launch_bounds__(256) void reduce_small_kernel(ReduceArgs a) {
+  constexpr int DPL = D / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;  // b * H_q + h
+  if (row >= static_cast<size_t>(a.num_seqs) * a.num_q_heads) return;
+  const int b = static_cast<int>(row / a.num_q_heads);
+  const int64_t ctx = max(a.context_lens[b], 0);
+  const int n = static_cast<int>(min<int64_t>((ctx + a.partition_size - 1) / a.partition_size,
+                                              min(a.max_partitions, MAXP)));
+  const float* lse_row = a.part_lse + row * a.max_partitions;
+  const float* out_row = a.part_out + row * a.max_partitions * D + lane * DPL;
+  const float my_lse = lane < n ? lse_row[lane] : kNegInf;
+  float o[MAXP][DPL];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[p][e] = 0.f;
+    if (p < n) {
+      if constexpr (DPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(out_row + static_cast<size_t>(p) * D);
+        o[p][0] = v.x;
+        o[p][1] = v.y;
+      } else {
+        o[p][0] = out_row[static_cast<size_t>(p) * D];
+      }
+    }
+  }
+  const float M = group_allreduce<64>(my_lse, OpMax());
+  float acc[DPL], wsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      if (p < n) {
+        const float lp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_lse), p));
+        const float w = fast_exp2((lp - M) * kLog2e);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, o[p][e], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const float v = M != kNegInf ? acc[e] / wsum : 0.f;
+    const size_t idx = row * D + lane * DPL + e;
+    if constexpr (BF) {
+      static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_bits(v);
+    } else {
+      static_cast<float*>(a.out)[idx] = v;
+    }
+  }
+  if (lane == 0) a.lse[row] = (M != kNegInf) ? M + __log2f(wsum) * kLn2 : kNegInf;
+}
+
+namespace {
+
+template <bool BF, int D>
+hipError_t launch_small(const ReduceArgs& a, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (a.max_partitions <= 8)
+    hipLaunchKernelGGL((reduce_small_kernel<BF, D, 8>), grid, dim3(256), 0, s, a);
+  else if (a.max_partitions <= 16)
+    hipLaunchKernelGGL((reduce_small_kernel<BF, D, 16>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((reduce_small_kernel<BF, D, 32>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_reduce(const ReduceArgs& a, DType dt, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.num_seqs) * a.num_q_heads));
   if (a.num_seqs == 0) return hipSuccess;
+  if (a.max_partitions <= 32 && (a.head_dim == 64 || a.head_dim == 128)) {
+    if (dt == DType::BF16)
+      return a.head_dim == 128 ? launch_small<true, 128>(a, s) : launch_small<true, 64>(a, s);
+    return a.head_dim == 128 ? launch_small<false, 128>(a, s) : launch_small<false, 64>(a, s);
+  }
   if (dt == DType::BF16) {
     if (a.head_dim == 128) hipLaunchKernelGGL((reduce_kernel<true, 128>), grid, dim3(256), 0, s, a);
     else if (a.head_dim == 64) hipLaunchKernelGGL((reduce_kernel<true, 64>), grid, dim3(256), 0, s, a);

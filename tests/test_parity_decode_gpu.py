@@ -105,7 +105,7 @@ def test_kv_write_empty_is_noop():
 # ---------------------------------------------------------------------------
 DECODE_CASES = {
     "tiny_f32": (1, {}, (0, 16, 32, 48)),
-    "llama3_8b_full": (2, {}, (0, 256, 512)),
+    "llama3_8b_full": (2, {}, (0, 32, 64, 128, 256, 512)),
     "llama2_70b_prefix_small": (4, dict(batch=16, ctx_min=512, ctx_max=1100, max_blocks_per_seq=35),
                                 (0, 512)),
     "long_split_small": (5, dict(batch=2, ctx_fixed=(4096, 3001), num_blocks=700,
