@@ -65,13 +65,10 @@ __device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int s) {
 // ---------------------------------------------------------------------------
 constexpr int kPN = 64;    // keys per K/V tile
 constexpr int kD = 128;
+// Lazy rescaling: a row keeps its running max until a tile's max exceeds it by
+// more than this (log2 units), so unnormalised probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
 
-#ifndef PA_PREFILL_NR
-#define PA_PREFILL_NR 2
-#endif
-#ifndef PA_PREFILL_RG
-#define PA_PREFILL_RG 1
-#endif
 #ifndef PA_PREFILL_BAND
 #define PA_PREFILL_BAND 1
 #endif
@@ -79,15 +76,26 @@ constexpr int kD = 128;
 // Wait until this wave's LDS-DMA loads have landed.
 __device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// NW waves per head-set (heads of one KV group), NR row-waves per head, RG
-// 16-row groups per wave: a workgroup covers 16*RG*NR query rows of NW heads.
-template <int NW, int NR, int RG>
-__global__ __launch_bounds__(64 * NW * NR) void prefill_mfma_kernel(PrefillArgs a, int group, int band, int ntiles) {
-  constexpr int NWAVES = NW * NR;
-  constexpr int PM = 16 * RG * NR;   // query rows per workgroup
-  // one K/V tile per buffer: K rows (64 x 16 chunks of 16 B) then V rows
-  __shared__ __attribute__((aligned(16))) u32x4 kv0[2048];
-  __shared__ __attribute__((aligned(16))) u32x4 kv1[2048];
+// Max / sum over lanes l, l^16, l^32, l^48 (the four key quarters of a query
+// column) with VALU lane swaps.
+template <class Op>
+__device__ __forceinline__ float quarter_reduce(float x, Op op) {
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// Four waves per workgroup: NW query heads of one KV group times 4/NW row
+// blocks; each wave owns 32 query rows (two 16-row groups) of one head, so a
+// K/V fragment read from LDS feeds two MFMAs.
+template <int NW>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int band, int ntiles) {
+  constexpr int NR = 4 / NW;
+  constexpr int PM = 32 * NR;   // query rows per workgroup
+  constexpr int RG = 2;         // 16-row groups per wave
+  // two K/V tiles: per tile K rows (64 x 16 chunks of 16 B) then V rows
+  __shared__ __attribute__((aligned(16))) u32x4 kvbuf[2 * 2048];
 
   // Workgroup -> (head column, sequence, q tile).  Workgroups are dealt to the
   // 8 XCDs round-robin, so the XCD is the id mod 8: head column c (KV head g,
@@ -114,17 +122,23 @@ __global__ __launch_bounds__(64 * NW * NR) void prefill_mfma_kernel(PrefillArgs 
   const SeqSpan sp = seq_span(a, s);
   const int qw0 = qt * PM;   // the workgroup's first row
   if (qw0 >= sp.len) return;
-  const int wave = NWAVES > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
   const int h = g * group + hb * NW + wave % NW;
-  const int q0 = qw0 + (wave / NW) * 16 * RG;   // this wave's first row
+  const int q0 = qw0 + (wave / NW) * 32;   // this wave's first row
   const int Hq = a.num_q_heads;
   constexpr int RC = kD * 2 / 16;   // 16-byte chunks per row
 
   const u32x4* qc = static_cast<const u32x4*>(a.q);
   const u32x4* kc = static_cast<const u32x4*>(a.k);
   const u32x4* vc = static_cast<const u32x4*>(a.v);
+
+  // Scores are reduced unscaled; a negative scale is folded into Q (exact
+  // sign flip of the bf16 values) so the max of raw scores is the max of
+  // scaled ones.
+  const float sl2 = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.
   bf16x8 qf[RG][4];
@@ -133,30 +147,32 @@ __global__ __launch_bounds__(64 * NW * NR) void prefill_mfma_kernel(PrefillArgs 
     const int row = q0 + 16 * rg + c16;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row < sp.len) w = qc[(static_cast<size_t>(sp.start + row) * Hq + h) * RC + 4 * c + j];
-      qf[rg][c] = __builtin_bit_cast(bf16x8, w);
+      u32x4 wq = {0u, 0u, 0u, 0u};
+      if (row < sp.len) wq = qc[(static_cast<size_t>(sp.start + row) * Hq + h) * RC + 4 * c + j] ^ qsign;
+      qf[rg][c] = __builtin_bit_cast(bf16x8, wq);
     }
   }
 
   const int kend = min(qw0 + PM, sp.len);   // keys 0 .. kend-1 are needed by the workgroup
   const int nkt = (kend + kPN - 1) / kPN;
 
-  // LDS-DMA of key tile kt: 2048 chunks (K then V), the NW waves take every
-  // NW-th 64-chunk slice.  Position p holds row (p%1024)/16 at stored chunk
-  // p%16; K chunks are XOR-swizzled by row%16 (conflict-free b128 reads of one
-  // dim chunk across 8 rows), V chunks by 2*(row%8) (conflict-free transposed
-  // reads).  Keys past the sequence read its last key (masked anyway).
+  // LDS-DMA of key tile kt: 2048 chunks (K then V); wave w issues slices
+  // w, w+4, ..., each 64 lanes x 16 B.  Slice i holds rows 4(i%16) + lane/16 at
+  // stored chunk lane%16; K chunks are XOR-swizzled by row%16 (conflict-free
+  // b128 reads of one dim chunk across rows), V chunks by 2*(row%8)
+  // (conflict-free transposed reads).  Keys past the sequence read its last
+  // key (masked anyway).
+  const int drow = 4 * wave + j;   // row of slice `wave`; later slices add 16
+  const int kchunk = c16 ^ (drow & 15);
+  const int vchunk = c16 ^ (2 * (drow & 7));
   auto issue = [&](int kt, u32x4* buf) {
-#pragma unroll 1
-    for (int i = wave; i < 32; i += NWAVES) {
-      const int p = 64 * i + lane;
-      const bool is_v = p >= 1024;
-      const int row = (p & 1023) >> 4, sc = p & 15;
-      const int chunk = is_v ? (sc ^ (2 * (row & 7))) : (sc ^ (row & 15));
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int row = drow + 16 * (ii & 3);
       const int key = min(kt * kPN + row, sp.len - 1);
-      const u32x4* src = (is_v ? vc : kc) + (static_cast<size_t>(sp.start + key) * Hkv + g) * RC + chunk;
-      global_to_lds16(src, &buf[64 * i]);
+      const size_t rowoff = (static_cast<size_t>(sp.start + key) * Hkv + g) * RC;
+      const u32x4* src = ii < 4 ? kc + rowoff + kchunk : vc + rowoff + vchunk;
+      global_to_lds16(src, &buf[64 * (wave + 4 * ii)]);
     }
   };
 
@@ -166,128 +182,138 @@ __global__ __launch_bounds__(64 * NW * NR) void prefill_mfma_kernel(PrefillArgs 
   for (int rg = 0; rg < RG; ++rg) {
     m[rg] = kNegInf;
     l[rg] = 0.f;
-  }
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  // transposed-read pieces: token rows 32kc + 4j + c16/4 (+16), dims 16dn + 4(c16%4)
+  // LDS byte offsets into kvbuf (tile 0; tile 1 adds 32 KB).
+  const char* lds = reinterpret_cast<const char*>(kvbuf);
+  uint32_t koff[4];   // K chunk (4c + j) ^ c16 of row c16 (+16 rows per nt)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) koff[c] = c16 * 256 + 16 * ((4 * c + j) ^ c16);
+  // transposed V reads: token row 4j + c16/4 (+32 per key chunk, +16 for the
+  // second half), dims 16dn + 4(c16%4), i.e. chunk 2dn + (c16%4)/2 stored at
+  // XOR 2*(row%8)
   const int tr_row = 4 * j + (c16 >> 2);
-  const int tr_half = (c16 & 3) >> 1;
-  const int tr_byte = 8 * (c16 & 1);
+  uint32_t voff[8];
+#pragma unroll
+  for (int dn = 0; dn < 8; ++dn)
+    voff[dn] = 16384 + tr_row * 256 + 32 * (dn ^ (tr_row & 7)) + 16 * ((c16 & 3) >> 1) + 8 * (c16 & 1);
 
-  auto compute = [&](int kt, const u32x4* buf) {
-    // S^T = K Q^T: four 16-key sub-tiles x two 16-row groups
+  auto tile = [&](int kt, bool masked) {
+    const uint32_t boff = (kt & 1) * 32768;
+    // S^T = K Q^T: sacc[nt][rg][i] = key kt*64 + 16nt + 4j + i, row q0 + 16rg + c16
     floatx4 sacc[4][RG];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      // keep each sub-tile's LDS reads next to their MFMAs (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) sacc[nt][rg] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int row = 16 * nt + c16;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x4 kw = buf[row * 16 + ((4 * c + j) ^ c16)];
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(lds + koff[c] + boff + 4096 * nt);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
           sacc[nt][rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[rg][c],
                                                                  sacc[nt][rg], 0, 0, 0);
       }
     }
-    // sacc[nt][rg][i]: key kt*64 + 16nt + 4j + i, query row q0 + 16rg + c16
-    const bool diag = kt * kPN + kPN - 1 > q0;
-    short4v pb[2][RG][2];   // [kc][rg][half]: P^T B operand pieces
+    bf16x8 pf[2][RG];   // P^T B operands: [key chunk of 32][rg]
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      const int qrow = q0 + 16 * rg + c16;
-      float mx = kNegInf;
+      if (masked) {
+        const int qrow = q0 + 16 * rg + c16;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv = sacc[nt][rg][i] * a.scale_log2;
-          if (diag && kt * kPN + 16 * nt + 4 * j + i > qrow) sv = kNegInf;
-          sacc[nt][rg][i] = sv;
-          mx = fmaxf(mx, sv);
-        }
+          for (int i = 0; i < 4; ++i)
+            if (kt * kPN + 16 * nt + 4 * j + i > qrow) sacc[nt][rg][i] = kNegInf;
       }
-      mx = across_rows(mx, OpMax());
-      const float m_new = fmaxf(m[rg], mx);
-      const float ms = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m[rg] - ms);
-      m[rg] = m_new;
+      float mx = fmaxf(sacc[0][rg][0], sacc[0][rg][1]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = (nt == 0 ? 2 : 0); i < 4; ++i) mx = fmaxf(mx, sacc[nt][rg][i]);
+      mx = quarter_reduce(mx, OpMax()) * sl2;
+      // lazy rescale: the whole wave moves its maxima only when some row's
+      // max has grown past the slack
+      const uint64_t grow = __builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack);
+      if (grow) {
+        const float m_new = fmaxf(m[rg], mx);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m[rg] - m_new);
+        m[rg] = m_new;
+        l[rg] *= alpha;
+#pragma unroll
+        for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
+      }
+      const float ms = m[rg] == kNegInf ? 0.f : m[rg];
       float ps = 0.f;
+      uint32_t pw[4][2];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
+        float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(sacc[nt][rg][i] - ms);
-          ps += p;
-          pb[nt >> 1][rg][nt & 1][i] = static_cast<short>(f32_to_bf16_bits(p));
+          float t = fmaf(sacc[nt][rg][i], sl2, -ms);
+          if (masked) t = sacc[nt][rg][i] == kNegInf ? kNegInf : t;
+          pv[i] = fast_exp2(t);
+          ps += pv[i];
         }
+        pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
+        pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
       }
-      l[rg] = l[rg] * alpha + ps;
 #pragma unroll
-      for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+        pf[kc2][rg] = __builtin_bit_cast(bf16x8, u32x4{pw[2 * kc2][0], pw[2 * kc2][1], pw[2 * kc2 + 1][0],
+                                                       pw[2 * kc2 + 1][1]});
+      l[rg] += ps;
     }
     // O^T += V^T P^T, 32 keys per MFMA: k-slot 8j+e <-> key 32kc + 4j + e (e<4),
     // 32kc + 16 + 4j + (e-4) (e>=4); V^T read transposed from the row-major tile.
-    const char* vbase = reinterpret_cast<const char*>(buf + 1024);
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
-      bf16x8 pfull[RG];
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
-        pfull[rg] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pb[kc2][rg][0], pb[kc2][rg][1],
-                                                                       0, 1, 2, 3, 4, 5, 6, 7));
-      const int r0 = 32 * kc2 + tr_row, r1 = r0 + 16;
 #pragma unroll
       for (int dn = 0; dn < 8; ++dn) {
-        if ((dn & 1) == 0) __builtin_amdgcn_sched_barrier(0);
-        const int ch = 2 * dn + tr_half;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(vbase + (r0 * 16 + (ch ^ (2 * (r0 & 7)))) * 16 + tr_byte));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(vbase + (r1 * 16 + (ch ^ (2 * (r1 & 7)))) * 16 + tr_byte));
+        typedef __attribute__((address_space(3))) short4v* lds_s4;
+        const char* va0 = lds + voff[dn] + boff + 8192 * kc2;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(va0));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(va0 + 4096));
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
-          oacc[rg][dn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfull[rg], oacc[rg][dn], 0, 0, 0);
+          oacc[rg][dn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[kc2][rg], oacc[rg][dn], 0, 0, 0);
       }
     }
   };
 
   // Double-buffered: the DMA of tile kt+1 runs while tile kt is computed.  A
   // buffer is refilled only after the barrier that follows its last reads.
-  issue(0, kv0);
-  for (int kt = 0; kt < nkt; kt += 2) {
+  // The wave's 32 rows (q0 is a multiple of 32) meet the diagonal in key tile
+  // q0/64 alone: earlier tiles need no mask, later ones are skipped (every
+  // wave still joins each barrier).
+  const int kt_diag = sp.len > q0 ? q0 / kPN : -1;   // -1: all rows are padding
+  issue(0, kvbuf);
+  for (int kt = 0; kt < nkt; ++kt) {
     wait_dma_all();
     __syncthreads();
-    if (kt + 1 < nkt) issue(kt + 1, kv1);
-    compute(kt, kv0);
-    if (kt + 1 >= nkt) break;
-    wait_dma_all();
-    __syncthreads();
-    if (kt + 2 < nkt) issue(kt + 2, kv0);
-    compute(kt + 1, kv1);
+    if (kt + 1 < nkt) issue(kt + 1, kvbuf + ((kt + 1) & 1) * 2048);
+    if (kt < kt_diag) tile(kt, false);
+    else if (kt == kt_diag) tile(kt, true);
   }
 
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const float lt = across_rows(l[rg], OpSum());
+    const float lt = quarter_reduce(l[rg], OpSum());
     const int row = q0 + 16 * rg + c16;
     if (row < sp.len) {
       const float inv = 1.f / lt;
       const size_t orow = static_cast<size_t>(sp.start + row) * Hq + h;
 #pragma unroll
       for (int dn = 0; dn < 8; ++dn) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[rg][dn][0] * inv, oacc[rg][dn][1] * inv);
-        w[1] = pack_bf16x2(oacc[rg][dn][2] * inv, oacc[rg][dn][3] * inv);
-        *reinterpret_cast<u32x2*>(out + orow * kD + 16 * dn + 4 * j) = w;
+        u32x2 wo;
+        wo[0] = pack_bf16x2(oacc[rg][dn][0] * inv, oacc[rg][dn][1] * inv);
+        wo[1] = pack_bf16x2(oacc[rg][dn][2] * inv, oacc[rg][dn][3] * inv);
+        *reinterpret_cast<u32x2*>(out + orow * kD + 16 * dn + 4 * j) = wo;
       }
       if (j == 0) a.lse[orow] = (m[rg] + __log2f(lt)) * kLn2;
     }
@@ -382,19 +408,18 @@ hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStrea
   const int group = a.num_q_heads / a.num_kv_heads;
   if (dt == DType::BF16 && head_dim == kD) {
     const int nw = group >= 4 ? 4 : group;   // heads of one KV group per workgroup
-    constexpr int kNR = PA_PREFILL_NR, kRG = PA_PREFILL_RG;
-    constexpr int kPM = 16 * kNR * kRG;
-    const int ntiles = (a.max_seqlen + kPM - 1) / kPM;
+    const int pm = 32 * (4 / nw);            // query rows per workgroup
+    const int ntiles = (a.max_seqlen + pm - 1) / pm;
     const int ncol = a.num_kv_heads * (group / nw);
     const int band = a.num_seqs < PA_PREFILL_BAND ? a.num_seqs : PA_PREFILL_BAND;
     const int64_t nb = (a.num_seqs + band - 1) / band;
     const int64_t n = 8LL * ((ncol + 7) / 8) * nb * band * ntiles;
-    if (n * 64 * nw * kNR > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
+    if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
     const dim3 grid(static_cast<unsigned>(n));
     switch (nw) {
-      case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, kNR, kRG>), grid, dim3(256 * kNR), 0, s, a, group, band, ntiles); break;
-      case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, kNR, kRG>), grid, dim3(128 * kNR), 0, s, a, group, band, ntiles); break;
-      default: hipLaunchKernelGGL((prefill_mfma_kernel<1, kNR, kRG>), grid, dim3(64 * kNR), 0, s, a, group, band, ntiles); break;
+      case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
+      case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
+      default: hipLaunchKernelGGL((prefill_mfma_kernel<1>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
     }
     return hipGetLastError();
   }

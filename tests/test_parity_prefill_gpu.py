@@ -31,6 +31,10 @@ PREFILL_CASES = {
     "single_seq": dict(num_seqs=1, lens_fixed=(257,)),
     "g8": dict(num_seqs=3, lens_fixed=(5, 100, 200), num_q_heads=16, num_kv_heads=2),
     "g1": dict(num_seqs=3, lens_fixed=(17, 64, 129), num_q_heads=4, num_kv_heads=4),
+    # one head per workgroup, four 32-row waves: rows past the wave's diagonal
+    # tile and waves wholly past the sequence end
+    "g1_long": dict(num_seqs=4, lens_fixed=(1, 40, 200, 333), num_q_heads=2, num_kv_heads=2),
+    "g2": dict(num_seqs=3, lens_fixed=(33, 96, 161), num_q_heads=8, num_kv_heads=4),
     "f32_d64": dict(dtype=wl.F32, num_seqs=4, lens_fixed=(1, 10, 33, 70), num_q_heads=4,
                     num_kv_heads=2, head_dim=64),
     "bf16_d64": dict(num_seqs=3, lens_fixed=(3, 40, 90), num_q_heads=4, num_kv_heads=2, head_dim=64),
@@ -56,6 +60,17 @@ def test_prefill_vector_kernel_matches_oracle(name):
         ops.set_force_vector_path(False)
     ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype)
     assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, name + " vector")
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0])
+def test_prefill_scale_sign_and_zero(scale):
+    # a negative scale reverses which key scores highest; zero gives the plain
+    # mean of the visible values
+    import dataclasses
+    case = dataclasses.replace(wl.make_case(3, **PREFILL_CASES["ragged_small"]), scale=scale)
+    out, lse = run_prefill(case)
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, f"scale={scale}")
 
 
 def test_prefill_row0_is_v0_bit_exact():
