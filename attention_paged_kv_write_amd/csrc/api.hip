@@ -143,6 +143,7 @@ int paged_attention_decode(void* out, float* lse, float* part_out, float* part_l
   a.num_partitions = num_parts;
   a.max_context_len = max_context_len;
   a.scale_log2 = scale * pa::kLog2e;
+  a.flat_units = 0;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s)

@@ -108,10 +108,12 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 // bytes land at lds_base + 16*l; lds_base must be wave-uniform.  Completion is
 // counted by vmcnt.  (A plain device function: called inside a lambda, the
 // builtin would also be instantiated for the host, where it does not exist.)
+// AUX is the cache-policy immediate (2: non-temporal, for data read once).
+template <int AUX = 0>
 __device__ __forceinline__ void global_to_lds16(const void* src, void* lds_base) {
   typedef __attribute__((address_space(3))) void* lds_ptr;
   typedef __attribute__((address_space(1))) void* gbl_ptr;
-  __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)lds_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((gbl_ptr)src, (lds_ptr)lds_base, 16, 0, AUX);
 }
 
 // 32-bit LDS byte address of a __shared__ object (for inline-asm DS operands).

@@ -26,6 +26,11 @@
 //    LPT lanes share a token row, dot products reduced with DPP.
 #include "kernels.h"
 
+// Cache policy of the K/V LDS-DMA loads (each cache byte is read once).
+#ifndef PA_DECODE_AUX
+#define PA_DECODE_AUX 2
+#endif
+
 namespace pa {
 
 namespace {
@@ -63,6 +68,60 @@ __device__ __forceinline__ Range work_range(const DecodeArgs& a, int b, int part
     r.blk_hi = nblk;
   }
   return r;
+}
+
+// Split-KV work unit u of a flat launch: the whole partitions of every
+// sequence (sequence by sequence), then the partial last partitions.  Full
+// units first keeps the long work at the head of the dispatch order, and a
+// grid with no empty units in front lets every CU take an even share of the
+// bytes.  One wave computes it (lane l scans sequences l*K .. l*K+K-1);
+// returns b = -1 past the last unit.  At most 64*16 sequences.
+struct Unit {
+  int b, part;
+};
+
+__device__ __forceinline__ Unit flat_unit(const DecodeArgs& a, int u) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.num_seqs;
+  const int per = a.partition_size;
+  const int cap = min(a.max_context_len, a.max_blocks_per_seq * a.block_size);
+  const int K = (B + 63) >> 6;
+  int nf = 0, np = 0;
+  for (int k = 0; k < K; ++k) {
+    const int sq = lane * K + k;
+    if (sq < B) {
+      const int ctx = clampi(a.context_lens[sq], 0, cap);
+      nf += ctx / per;
+      np += (ctx % per) != 0;
+    }
+  }
+  // inclusive scans of the per-lane counts
+  int sf = nf, sp = np;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int tf = __shfl_up(sf, d), tp = __shfl_up(sp, d);
+    if (lane >= d) {
+      sf += tf;
+      sp += tp;
+    }
+  }
+  const int F = __builtin_amdgcn_readlane(sf, 63), P = __builtin_amdgcn_readlane(sp, 63);
+  const bool full = u < F;
+  if (!full && u >= F + P) return Unit{-1, 0};
+  const int v = full ? u : u - F;
+  const int incl = full ? sf : sp;
+  // the lane whose range holds unit v, and the units before it
+  const int owner = __popcll(__builtin_amdgcn_ballot_w64(incl <= v));
+  const int excl = owner > 0 ? __shfl(incl, owner - 1) : 0;
+  int rem = v - excl;
+  for (int k = 0; k < K; ++k) {
+    const int sq = owner * K + k;
+    const int ctx = sq < B ? clampi(a.context_lens[sq], 0, cap) : 0;
+    const int n = full ? ctx / per : ((ctx % per) != 0);
+    if (rem < n) return Unit{sq, full ? rem : ctx / per};
+    rem -= n;
+  }
+  return Unit{-1, 0};
 }
 
 // Final cross-wave merge of (m, l, acc) held in LDS and the store of the result.
@@ -334,7 +393,18 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   __shared__ float sm_l[W][G];
   __shared__ float sm_acc[W > 1 ? W : 1][G][D];
 
-  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  int g, b, part;
+  if (W == 1 && a.flat_units) {
+    g = blockIdx.x % a.num_kv_heads;
+    const Unit un = flat_unit(a, blockIdx.x / a.num_kv_heads);
+    if (un.b < 0) return;
+    b = __builtin_amdgcn_readfirstlane(un.b);
+    part = __builtin_amdgcn_readfirstlane(un.part);
+  } else {
+    g = blockIdx.x;
+    b = blockIdx.y;
+    part = blockIdx.z;
+  }
   const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
@@ -420,13 +490,13 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int tok = 4 * c + j;   // row-major: 16 lanes per 256-byte row
-        global_to_lds16(kc + base + tok * RC + (c16 ^ tok), &ring[wave][slot][64 * c]);
+        global_to_lds16<PA_DECODE_AUX>(kc + base + tok * RC + (c16 ^ tok), &ring[wave][slot][64 * c]);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int tok = 4 * k + j;
         const u32x4* src = vc + base + tok * RC + (c16 ^ (2 * (tok & 7)));
-        global_to_lds16(src, &ring[wave][slot][256 + 64 * k]);
+        global_to_lds16<PA_DECODE_AUX>(src, &ring[wave][slot][256 + 64 * k]);
       }
     };
 
@@ -562,9 +632,16 @@ namespace {
 
 template <int G, int BS>
 hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  if (a.partition_size > 0)
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, PA_DECODE_SLOTS>), grid, dim3(64), 0, s, a);
-  else
+  if (a.partition_size > 0) {
+    // flat grid of balanced units (one per KV head and live partition, in the
+    // order flat_unit defines; the kernel maps ids past the last unit to no
+    // work), unit-major so the KV heads of a unit spread over the XCDs
+    DecodeArgs f = a;
+    const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
+    f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
+    const dim3 fg = f.flat_units ? dim3(grid.x * grid.y * grid.z) : grid;
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, PA_DECODE_SLOTS>), fg, dim3(64), 0, s, f);
+  } else
     hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, PA_DECODE_SLOTS>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

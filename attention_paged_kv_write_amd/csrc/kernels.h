@@ -41,6 +41,7 @@ struct DecodeArgs {
   int num_partitions;    // partition dimension of part_* (1 when single pass)
   int max_context_len;
   float scale_log2;      // scale * log2(e)
+  int flat_units;        // split-KV MFMA kernel: 1-D grid of balanced work units
 };
 
 struct ReduceArgs {

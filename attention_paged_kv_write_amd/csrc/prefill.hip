@@ -69,10 +69,6 @@ constexpr int kD = 128;
 // more than this (log2 units), so unnormalised probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
 
-#ifndef PA_PREFILL_BAND
-#define PA_PREFILL_BAND 1
-#endif
-
 // Wait until this wave's LDS-DMA loads have landed.
 __device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -90,7 +86,7 @@ __device__ __forceinline__ float quarter_reduce(float x, Op op) {
 // blocks; each wave owns 32 query rows (two 16-row groups) of one head, so a
 // K/V fragment read from LDS feeds two MFMAs.
 template <int NW>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int band, int ntiles) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int ntiles) {
   constexpr int NR = 4 / NW;
   constexpr int PM = 32 * NR;   // query rows per workgroup
   constexpr int RG = 2;         // 16-row groups per wave
@@ -99,10 +95,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 
   // Workgroup -> (head column, sequence, q tile).  Workgroups are dealt to the
   // 8 XCDs round-robin, so the XCD is the id mod 8: head column c (KV head g,
-  // head block hb) lives on XCD c mod 8, and its workgroups run through bands
-  // of `band` sequences, q tiles longest-first inside a band with the band's
-  // sequences interleaved.  Workgroups of one band run together on one XCD
-  // and stream the same K/V prefix through its L2.
+  // head block hb) lives on XCD c mod 8, and its workgroups run sequence by
+  // sequence, q tiles longest-first within a sequence.  Concurrent workgroups
+  // of an XCD thus stream the same K/V prefix through its L2.
   const int Hkv = a.num_kv_heads;
   const int nhb = group / NW;   // head blocks per KV group
   const int ncol = Hkv * nhb;
@@ -114,14 +109,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   r /= cpx;
   if (col >= ncol) return;
   const int g = col % Hkv, hb = col / Hkv;
-  const int per_band = band * ntiles;
-  const int bi = r / per_band, w = r % per_band;
-  const int s = bi * band + w % band;
+  const int s = r / ntiles, w = r % ntiles;
   if (s >= a.num_seqs) return;
-  const int qt = ntiles - 1 - w / band;
   const SeqSpan sp = seq_span(a, s);
+  const int qt = (sp.len + PM - 1) / PM - 1 - w;
+  if (qt < 0) return;
   const int qw0 = qt * PM;   // the workgroup's first row
-  if (qw0 >= sp.len) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
@@ -411,15 +404,13 @@ hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStrea
     const int pm = 32 * (4 / nw);            // query rows per workgroup
     const int ntiles = (a.max_seqlen + pm - 1) / pm;
     const int ncol = a.num_kv_heads * (group / nw);
-    const int band = a.num_seqs < PA_PREFILL_BAND ? a.num_seqs : PA_PREFILL_BAND;
-    const int64_t nb = (a.num_seqs + band - 1) / band;
-    const int64_t n = 8LL * ((ncol + 7) / 8) * nb * band * ntiles;
+    const int64_t n = 8LL * ((ncol + 7) / 8) * a.num_seqs * ntiles;
     if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
     const dim3 grid(static_cast<unsigned>(n));
     switch (nw) {
-      case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
-      case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
-      default: hipLaunchKernelGGL((prefill_mfma_kernel<1>), grid, dim3(256), 0, s, a, group, band, ntiles); break;
+      case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4>), grid, dim3(256), 0, s, a, group, ntiles); break;
+      case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2>), grid, dim3(256), 0, s, a, group, ntiles); break;
+      default: hipLaunchKernelGGL((prefill_mfma_kernel<1>), grid, dim3(256), 0, s, a, group, ntiles); break;
     }
     return hipGetLastError();
   }
