@@ -318,19 +318,23 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   merge_and_store<BF, D, G>(a, b, g, part, sm_m, sm_l, sm_acc);
 }
 
-// Read one decode tile back from its LDS slot: wait until at most VMCNT
-// LDS-DMA loads (those of the newer slots) are still in flight, issue the four
-// lane-linear 16-byte K reads and the eight transposed V reads, and wait for
-// them.  Written as one asm block because the compiler cannot count LDS-DMA
-// completions across the ring and would otherwise drain every load in flight.
-// The asm exists only in the device pass (its register constraints are
-// meaningless to the host compiler).
-template <int VMCNT>
+// Wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+#endif
+}
+
+// Read one decode tile back from its LDS slot: the four lane-linear 16-byte K
+// reads and the eight transposed V reads, then wait for them.  Inline asm (only
+// in the device pass: its register constraints mean nothing to the host
+// compiler) so that the compiler, which cannot track LDS-DMA completions, adds
+// no wait of its own for the DMA loads in flight.
 __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const uint32_t* k_addr,
                                                      const uint32_t* v_addr, uint32_t off) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile(
-      "s_waitcnt vmcnt(%24)\n\t"
       "ds_read_b128 %0, %12\n\t"
       "ds_read_b128 %1, %13\n\t"
       "ds_read_b128 %2, %14\n\t"
@@ -348,8 +352,7 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
         "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]), "=&v"(vt[6]), "=&v"(vt[7])
       : "v"(k_addr[0] + off), "v"(k_addr[1] + off), "v"(k_addr[2] + off), "v"(k_addr[3] + off),
         "v"(v_addr[0] + off), "v"(v_addr[1] + off), "v"(v_addr[2] + off), "v"(v_addr[3] + off),
-        "v"(v_addr[4] + off), "v"(v_addr[5] + off), "v"(v_addr[6] + off), "v"(v_addr[7] + off),
-        "i"(VMCNT)
+        "v"(v_addr[4] + off), "v"(v_addr[5] + off), "v"(v_addr[6] + off), "v"(v_addr[7] + off)
       : "memory");
 #endif
 }
@@ -363,9 +366,9 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
 // sequence's blocks round-robin and meet in LDS).
 //
 // Per 16-token tile of KV head g:
-//   S^T[16 tok x 16 col] = K[16 x 128] . Q^T   four v_mfma_f32_16x16x32_bf16; K
-//       comes straight from HBM into the A operand (lane (j, c16): token c16,
-//       dims 32c + 8j), the group's query heads are the B operand columns.
+//   S^T[16 tok x 16 col] = K[16 x 128] . Q^T   four v_mfma_f32_16x16x32_bf16;
+//       lane (j, c16) reads token c16, dims 32c + 8j of the K tile as its A
+//       operand, the group's query heads are the B operand columns.
 //   online softmax on S^T: lane (j, c16) holds tokens 4j..4j+3 of column c16,
 //       so the running max/rescale of a column stay in its own lanes; the tile
 //       max needs one exchange across the four 16-lane rows.
@@ -374,11 +377,13 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
 //       tokens of one column per lane), and V^T comes from LDS through
 //       ds_read_b64_tr_b16, which hands each lane 4 consecutive tokens of one
 //       dim from a row-major V tile.
-// V tiles reach LDS by global_load_lds_dwordx4 (no VGPRs), three slots per
-// wave, so two tiles are in flight while one is computed.  Lane l of load k
-// fetches 16 bytes of token 4k + l/16, chunk (l%16) ^ 2*(token%8): the XOR
-// spreads the eight tokens a transposed read touches over all 64 banks.
-template <int G, int BS, int W, int NS>
+// K and V tiles reach LDS by non-temporal global_load_lds_dwordx4 (no VGPRs;
+// every cache byte is read once) into a two-slot ring per wave, so one tile's
+// loads are in flight while the other is computed.  Both tiles are stored
+// row-major with XOR-swizzled 16-byte chunks: K chunk q of token t at q ^ t
+// (conflict-free lane-linear b128 reads), V at q ^ 2*(t%8) (the eight tokens a
+// transposed read touches spread over all 64 banks).
+template <int G, int BS, int W>
 __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int RC = D * 2 / 16;   // 16-byte chunks per row (16)
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   // LDS ring, per slot and wave: K tile (4 KB, MFMA A layout, lane-linear)
   // then V tile (4 KB, row-major, chunk-swizzled)
   constexpr int kSlotBytes = 512 * 16;
-  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][512];
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][2][512];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
   __shared__ float sm_acc[W > 1 ? W : 1][G][D];
@@ -472,24 +477,27 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
     if (w0 > 0) ids = load_ids(w0);
     const int wn = min(64, n_blocks - w0);
     const int nt = wn * TPB;
-    int p0 = 0, p1 = 0, p2 = 0, l0 = 0, l1 = 0, l2 = 0;
 
-    // Issue the loads of window tile n into an LDS slot: K in MFMA A layout
-    // (lane (j, c16) brings token c16, dims 32c + 8j; read back by the same
-    // lane), V row-major with the XOR chunk swizzle.  A block id outside the
-    // pool (a precondition violation) reads block 0 with every token masked.
-    auto fetch = [&](int n, int slot, int& pos0, int& lim) {
+    // Window tile n: first token position and the valid-token limit (0 when
+    // the block id lies outside the pool, a precondition violation: block 0 is
+    // read instead and every token masked).
+    auto tile_span = [&](int n, int& pos0, int& lim, int& phys) {
       const int i = n / TPB;
-      const int tile = n % TPB;
-      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + tile * 16;
-      int phys = __builtin_amdgcn_readlane(ids, i);
+      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + (n % TPB) * 16;
+      phys = __builtin_amdgcn_readlane(ids, i);
       const bool ok = phys >= 0 && phys < a.num_blocks;
       phys = ok ? phys : 0;
       lim = ok ? r.ctx : 0;
-      const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + tile * 16) * RC;
+    };
+    // Issue the LDS-DMA loads of window tile n into a ring slot (K then V, both
+    // row-major with the XOR chunk swizzle).
+    auto fetch = [&](int n, int slot) {
+      int pos0, lim, phys;
+      tile_span(n, pos0, lim, phys);
+      const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int tok = 4 * c + j;   // row-major: 16 lanes per 256-byte row
+        const int tok = 4 * c + j;   // 16 lanes per 256-byte row
         global_to_lds16<PA_DECODE_AUX>(kc + base + tok * RC + (c16 ^ tok), &ring[wave][slot][64 * c]);
       }
 #pragma unroll
@@ -500,16 +508,14 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       }
     };
 
-    auto process = [&](int slot, int pos0, int lim) {
+    // Compute window tile n from its ring slot (its loads have landed).
+    auto process = [&](int n, int slot) {
+      int pos0, lim, phys;
+      tile_span(n, pos0, lim, phys);
       const uint32_t off = slot * kSlotBytes;
-      // The slot's tile is read back in one block: wait until only the two
-      // newer slots' 16 LDS-DMA loads may still be in flight, read K (four
-      // lane-linear 16-byte reads) and V^T (eight transposed reads), and wait
-      // for the reads.  The compiler cannot count LDS-DMA completions across
-      // the ring, so it would otherwise drain every load in flight here.
       u32x4 kw[4];
       u32x2 vt[8];
-      lds_read_decode_tile<8 * (NS - 1)>(kw, vt, k_addr, v_addr, off);
+      lds_read_decode_tile(kw, vt, k_addr, v_addr, off);
       floatx4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -552,36 +558,22 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       }
     };
 
-    // Three-slot ring, unrolled so each slot is a distinct LDS array.  Fetches
-    // are unconditional (clamped to the last tile, an L2-hot reload) so every
-    // path through the loop has the same loads in flight.
-    if constexpr (NS == 3) {
-      fetch(0, 0, p0, l0);
-      fetch(min(1, nt - 1), 1, p1, l1);
-      for (int n = 0; n < nt; n += 3) {
-        fetch(min(n + 2, nt - 1), 2, p2, l2);
-        process(0, p0, l0);
-        fetch(min(n + 3, nt - 1), 0, p0, l0);
-        if (n + 1 < nt) process(1, p1, l1);
-        fetch(min(n + 4, nt - 1), 1, p1, l1);
-        if (n + 2 < nt) process(2, p2, l2);
+    // Two-slot ring: tile n+1's loads are issued before tile n is computed;
+    // the wait then lets exactly those 8 loads stay in flight (none after the
+    // last tile, so no tile is fetched twice).  The compiler cannot count
+    // LDS-DMA completions, so the waits are explicit.
+    fetch(0, 0);
+    for (int n = 0; n < nt; ++n) {
+      const int slot = n & 1;
+      if (n + 1 < nt) {
+        fetch(n + 1, slot ^ 1);
+        wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
       }
-    } else {
-      fetch(0, 0, p0, l0);
-      for (int n = 0; n < nt; n += 2) {
-        fetch(min(n + 1, nt - 1), 1, p1, l1);
-        process(0, p0, l0);
-        fetch(min(n + 2, nt - 1), 0, p0, l0);
-        if (n + 1 < nt) process(1, p1, l1);
-      }
-      (void)p2;
-      (void)l2;
+      process(n, slot);
     }
   }
-  // LDS-DMA writes still in flight (the clamped reloads) must land before the
-  // workgroup's LDS is reused or released.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
   l = across_rows(l, OpSum());
   if constexpr (W == 1) {
     if (c16 >= G) return;
@@ -626,10 +618,6 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 // ---------------------------------------------------------------------------
 namespace {
 
-#ifndef PA_DECODE_SLOTS
-#define PA_DECODE_SLOTS 2
-#endif
-
 template <int G, int BS>
 hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.partition_size > 0) {
@@ -640,9 +628,9 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
     const dim3 fg = f.flat_units ? dim3(grid.x * grid.y * grid.z) : grid;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, PA_DECODE_SLOTS>), fg, dim3(64), 0, s, f);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1>), fg, dim3(64), 0, s, f);
   } else
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, PA_DECODE_SLOTS>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
