@@ -36,7 +36,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 DECODE_SOURCES = ("attention_paged_kv_write_amd/csrc/decode.hip",
                   "attention_paged_kv_write_amd/csrc/common.h",
                   "attention_paged_kv_write_amd/csrc/kernels.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.txt")
+PREFILL_SOURCES = ("attention_paged_kv_write_amd/csrc/prefill.hip",
+                   "attention_paged_kv_write_amd/csrc/common.h",
+                   "attention_paged_kv_write_amd/csrc/kernels.h")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_llama3_8b.txt")
 
 
 def log(msg):
@@ -51,15 +55,15 @@ def source_digest(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(bytes_per_launch_alg):
-    """HBM bytes per decode launch from committed rocprofv3 counters, if the
-    decode kernel source is unchanged since they were taken; else None."""
+def measured_traffic(path, sources):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counters, if
+    the kernel's sources are unchanged since they were taken; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != source_digest(DECODE_SOURCES):
+    if t.get("kernel_source_sha256") != source_digest(sources):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -178,11 +182,11 @@ def main(argv=None):
     kv_bytes = int(case.context_lens.astype(np.int64).sum()) * Hkv * 2 * d * 2
     value_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved_gbs = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(kv_bytes)
+    traffic = measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
     roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "decode_mfma_kernel<G=4,BS=16,W=1,NS=2> (paged_attention_decode)",
+                "kernel": "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode)",
                 "kernel_avg_us": round(dec_avg_ms * 1e3, 2),
                 "kernel_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                 "kernel_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
@@ -200,6 +204,9 @@ def main(argv=None):
         log(f"prefill workload generated in {time.perf_counter() - t0:.1f}s: T={pc.total_tokens}")
         lens = np.diff(pc.cu_seqlens).astype(np.int64)
         flops = 4.0 * pc.spec.head_dim * pc.spec.num_q_heads * float((lens * (lens + 1) // 2).sum())
+        # q, k, v read once; out and lse written once
+        T_, Hq_, Hkv_, d_ = pc.total_tokens, pc.spec.num_q_heads, pc.spec.num_kv_heads, pc.spec.head_dim
+        io_bytes = T_ * (2 * Hq_ + 2 * Hkv_) * d_ * 2 + T_ * Hq_ * 4
         pq, pk, pv, pcu = up(pc.q), up(pc.k), up(pc.v), up(pc.cu_seqlens)
         pout = torch.empty_like(pq)
         plse = torch.empty((pc.total_tokens, pc.spec.num_q_heads), dtype=torch.float32, device=dev)
@@ -231,7 +238,10 @@ def main(argv=None):
                    "kernel_avg_us": round(pms * 1e3, 1), "tflops": round(tflops, 1),
                    "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                                "traffic": None, "algorithmic_flops_per_launch": flops},
+                                "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
+                                "kernel": "prefill_mfma_kernel<NW=4> (varlen_causal_prefill)",
+                                "algorithmic_flops_per_launch": flops,
+                                "algorithmic_bytes_per_launch": io_bytes},
                    "kv_write": {"kernel_avg_us": round(wms * 1e3, 1),
                                 "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)}}
         log(f"prefill {pms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; prompt kv write {wms * 1e3:.1f} us")
