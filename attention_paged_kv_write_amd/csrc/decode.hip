@@ -9,19 +9,18 @@
 // sum, rescaled accumulator) so scores never leave registers, the IO-aware
 // fusion the FlashAttention sections of those pages describe.
 //
-// Work unit: one workgroup (4 waves) per (sequence, KV head, partition).  The
-// waves of a workgroup take the partition's blocks round-robin, each keeping
-// its own softmax state; the four states are merged through LDS at the end.
-// The work split depends only on logical positions, never on physical block
-// ids, so permuting the pool leaves every result bit-identical.
+// Work units: with a partition size, one wave per (KV head, sequence,
+// partition), the partial results merged by paged_attention_reduce; without,
+// one workgroup of four waves per (KV head, sequence) that take the blocks
+// round-robin and merge their softmax states through LDS.  The work split
+// depends only on logical positions, never on physical block ids, so
+// permuting the pool leaves every result bit-identical.
 //
 // Two kernels:
-//  * decode_mfma_kernel (bf16, head_dim 128): QK^T of a 16-token tile against
-//    the whole GQA group is one chain of four v_mfma_f32_16x16x32_bf16 (K tile
-//    as the A operand, straight from HBM in MFMA layout; the group's query
-//    heads as the B operand, zero-padded to 16 columns).  P.V runs on the
-//    vector ALU from 16-byte V row loads, the probabilities handed over
-//    through LDS.
+//  * decode_mfma_kernel (bf16, head_dim 128): K and V tiles of 16 tokens are
+//    staged in LDS by LDS-DMA; QK^T against the whole GQA group is a chain of
+//    four v_mfma_f32_16x16x32_bf16 and P.V eight v_mfma_f32_16x16x16_bf16 (see
+//    the comment above the kernel).
 //  * decode_generic_kernel (fp32 or bf16, head_dim 64/128): vector ALU only;
 //    LPT lanes share a token row, dot products reduced with DPP.
 #include "kernels.h"
