@@ -133,19 +133,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const float sl2 = fabsf(a.scale_log2);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.
-  bf16x8 qf[RG][4];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int row = q0 + 16 * rg + c16;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 wq = {0u, 0u, 0u, 0u};
-      if (row < sp.len) wq = qc[(static_cast<size_t>(sp.start + row) * Hq + h) * RC + 4 * c + j] ^ qsign;
-      qf[rg][c] = __builtin_bit_cast(bf16x8, wq);
-    }
-  }
-
+  bf16x8 qf[RG][4];   // Q^T B operands, loaded below (after the first tile is requested)
   const int kend = min(qw0 + PM, sp.len);   // keys 0 .. kend-1 are needed by the workgroup
   const int nkt = (kend + kPN - 1) / kPN;
 
@@ -284,7 +272,28 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // q0/64 alone: earlier tiles need no mask, later ones are skipped (every
   // wave still joins each barrier).
   const int kt_diag = sp.len > q0 ? q0 / kPN : -1;   // -1: all rows are padding
-  issue(0, kvbuf);
+  issue(0, kvbuf);   // the first tile's loads overlap the Q loads
+
+  // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.  Rows past
+  // the sequence load its last row (all eight loads in flight at once) and are
+  // zeroed afterwards.
+  u32x4 qw[RG][4];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int row = min(q0 + 16 * rg + c16, sp.len - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qw[rg][c] = qc[(static_cast<size_t>(sp.start + row) * Hq + h) * RC + 4 * c + j];
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const bool live = q0 + 16 * rg + c16 < sp.len;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      qf[rg][c] = __builtin_bit_cast(bf16x8, live ? (qw[rg][c] ^ qsign) : zero);
+    }
+  }
+
   for (int kt = 0; kt < nkt; ++kt) {
     wait_dma_all();
     __syncthreads();
