@@ -196,6 +196,34 @@ def main(argv=None):
     del copies
     torch.cuda.empty_cache()
 
+    # Practical HBM ceiling on this machine: a plain 1 GiB device copy (read + write).
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    src.zero_()
+    f32 = src.view(torch.float32)
+    f32.sum()
+    ca.record(stream)
+    for _ in range(5):
+        f32.sum()
+    cb.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = nb * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    stream_ceiling = {"kind": "torch on 1 GiB: device copy (read + write bytes) and fp32 sum (read bytes)",
+                      "copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
+                      "frac_of_peak": round(max(copy_gbs, read_gbs) / HBM_PEAK_GBS, 4)}
+    log(f"device copy {copy_gbs:.0f} GB/s, sum {read_gbs:.0f} GB/s")
+    del src, dst
+    torch.cuda.empty_cache()
+
     # ----------------------------------------------------------------- prefill
     prefill = None
     if not args.no_prefill:
@@ -242,6 +270,7 @@ def main(argv=None):
                                 "kernel": "prefill_mfma_kernel<NW=4> (varlen_causal_prefill)",
                                 "algorithmic_flops_per_launch": flops,
                                 "algorithmic_bytes_per_launch": io_bytes},
+                   "tokens_per_s": round(pc.total_tokens / (pms * 1e-3), 1),
                    "kv_write": {"kernel_avg_us": round(wms * 1e3, 1),
                                 "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)}}
         log(f"prefill {pms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; prompt kv write {wms * 1e3:.1f} us")
@@ -297,6 +326,8 @@ def main(argv=None):
                    "step": "paged_kv_write(64 tokens) + paged_attention_decode + paged_attention_reduce",
                    "kv_bytes_per_step": kv_bytes},
         "roofline": roofline,
+        "decode_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "stream_ceiling": stream_ceiling,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }
