@@ -72,6 +72,26 @@ constexpr float kRescaleSlack = 8.f;
 // Wait until this wave's LDS-DMA loads have landed.
 __device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// max(a, b, c) as one v_max3_f32, without the NaN-quieting copies the
+// compiler puts in front of fmaxf on matrix-core results.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(b, c));
+#endif
+}
+
+// Max over lanes l, l^16, l^32, l^48 (the four key quarters of a query column).
+__device__ __forceinline__ float quarter_max(float x) {
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = vmax3(__uint_as_float(p16[0]), __uint_as_float(p16[1]), __uint_as_float(p16[1]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return vmax3(__uint_as_float(p32[0]), __uint_as_float(p32[1]), __uint_as_float(p32[1]));
+}
+
 // Max / sum over lanes l, l^16, l^32, l^48 (the four key quarters of a query
 // column) with VALU lane swaps.
 template <class Op>
@@ -209,36 +229,39 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
           for (int i = 0; i < 4; ++i)
             if (kt * kPN + 16 * nt + 4 * j + i > qrow) sacc[nt][rg][i] = kNegInf;
       }
-      float mx = fmaxf(sacc[0][rg][0], sacc[0][rg][1]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = (nt == 0 ? 2 : 0); i < 4; ++i) mx = fmaxf(mx, sacc[nt][rg][i]);
-      mx = quarter_reduce(mx, OpMax()) * sl2;
+      // row max of the raw scores
+      float mx = vmax3(vmax3(sacc[0][rg][0], sacc[0][rg][1], sacc[0][rg][2]),
+                       vmax3(sacc[0][rg][3], sacc[1][rg][0], sacc[1][rg][1]),
+                       vmax3(sacc[1][rg][2], sacc[1][rg][3], sacc[2][rg][0]));
+      mx = vmax3(mx, vmax3(sacc[2][rg][1], sacc[2][rg][2], sacc[2][rg][3]),
+                 vmax3(sacc[3][rg][0], sacc[3][rg][1], vmax3(sacc[3][rg][2], sacc[3][rg][3], sacc[3][rg][3])));
+      mx = quarter_max(mx) * sl2;
       // lazy rescale: the whole wave moves its maxima only when some row's
-      // max has grown past the slack
+      // max has grown past the slack.  Every processed tile holds at least one
+      // visible key of every row, so mx is finite and the first tile always
+      // moves m off -inf (alpha = 0 then).
       const uint64_t grow = __builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack);
       if (grow) {
         const float m_new = fmaxf(m[rg], mx);
-        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m[rg] - m_new);
+        const float alpha = fast_exp2(m[rg] - m_new);
         m[rg] = m_new;
         l[rg] *= alpha;
 #pragma unroll
         for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
       }
-      const float ms = m[rg] == kNegInf ? 0.f : m[rg];
-      float ps = 0.f;
+      const float nm = -m[rg];
       uint32_t pw[4][2];
+      float ps[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float t = fmaf(sacc[nt][rg][i], sl2, -ms);
+          float t = fmaf(sacc[nt][rg][i], sl2, nm);
           if (masked) t = sacc[nt][rg][i] == kNegInf ? kNegInf : t;
           pv[i] = fast_exp2(t);
-          ps += pv[i];
         }
+        ps[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
         pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
       }
@@ -246,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       for (int kc2 = 0; kc2 < 2; ++kc2)
         pf[kc2][rg] = __builtin_bit_cast(bf16x8, u32x4{pw[2 * kc2][0], pw[2 * kc2][1], pw[2 * kc2 + 1][0],
                                                        pw[2 * kc2 + 1][1]});
-      l[rg] += ps;
+      l[rg] += (ps[0] + ps[1]) + (ps[2] + ps[3]);   // this lane's quarter of the row sum, fp32
     }
     // O^T += V^T P^T, 32 keys per MFMA: k-slot 8j+e <-> key 32kc + 4j + e (e<4),
     // 32kc + 16 + 4j + (e-4) (e>=4); V^T read transposed from the row-major tile.
