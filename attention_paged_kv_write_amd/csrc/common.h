@@ -19,6 +19,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Lazy rescaling: a softmax row keeps its running max until a tile's max
+// exceeds it by more than this (log2 units), so unnormalised probabilities stay
+// below 2^8; the result is unchanged (numerator and denominator share the max).
+constexpr float kRescaleSlack = 8.f;
 
 // ---------------------------------------------------------------------------
 // bf16 <-> f32 on raw bit patterns
@@ -97,6 +101,26 @@ __device__ __forceinline__ float across_rows(float x, Op op) {
   x = op(x, swz_xor16(x));
   x = op(x, xchg_xor32(x));
   return x;
+}
+
+// max(a, b, c) as one v_max3_f32, without the NaN-quieting copies the
+// compiler puts in front of fmaxf on matrix-core results.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+#else
+  return fmaxf(a, fmaxf(b, c));
+#endif
+}
+
+// Max over lanes l, l^16, l^32, l^48 (the four key quarters of a query column).
+__device__ __forceinline__ float quarter_max(float x) {
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = vmax3(__uint_as_float(p16[0]), __uint_as_float(p16[1]), __uint_as_float(p16[1]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return vmax3(__uint_as_float(p32[0]), __uint_as_float(p32[1]), __uint_as_float(p32[1]));
 }
 
 // exp2 that treats a -inf argument exactly (hardware v_exp_f32).

@@ -521,28 +521,25 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[c]), qf[c], st, 0, 0, 0);
       // st[i]: score of token pos0 + 4j + i for column c16
       float s[4];
-      float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = (pos0 + 4 * j + i < lim) ? st[i] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, s[i]);
+      for (int i = 0; i < 4; ++i) s[i] = (pos0 + 4 * j + i < lim) ? st[i] * a.scale_log2 : kNegInf;
+      const float mx = quarter_max(vmax3(vmax3(s[0], s[1], s[2]), s[3], s[3]));
+      // lazy rescale: the running max moves (with l and O) only when some
+      // column's tile max exceeds it by more than the slack
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int dn = 0; dn < 8; ++dn) oacc[dn] *= alpha;
       }
-      mx = across_rows(mx, OpMax());
-      const float m_new = fmaxf(m, mx);
-      const float ms = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m - ms);
-      m = m_new;
-      short4v pb;
-      float ps = 0.f;
+      const float ms = m == kNegInf ? 0.f : m;   // no visible token yet (bad block ids)
+      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[i] - ms);
-        ps += p;
-        pb[i] = static_cast<short>(f32_to_bf16_bits(p));
-      }
-      l = l * alpha + ps;
-#pragma unroll
-      for (int dn = 0; dn < 8; ++dn) oacc[dn] *= alpha;
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - ms);
+      l += (p[0] + p[1]) + (p[2] + p[3]);
+      const short4v pb = __builtin_bit_cast(short4v, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
       // tokens past the end may hold anything (NaN): their V entries are
       // zero-selected, since a zero probability times NaN is still NaN
       const bool tail = pos0 + 16 > lim;

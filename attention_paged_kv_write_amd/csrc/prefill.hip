@@ -65,32 +65,9 @@ __device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int s) {
 // ---------------------------------------------------------------------------
 constexpr int kPN = 64;    // keys per K/V tile
 constexpr int kD = 128;
-// Lazy rescaling: a row keeps its running max until a tile's max exceeds it by
-// more than this (log2 units), so unnormalised probabilities stay below 2^8.
-constexpr float kRescaleSlack = 8.f;
 
 // Wait until this wave's LDS-DMA loads have landed.
 __device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// max(a, b, c) as one v_max3_f32, without the NaN-quieting copies the
-// compiler puts in front of fmaxf on matrix-core results.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-#else
-  return fmaxf(a, fmaxf(b, c));
-#endif
-}
-
-// Max over lanes l, l^16, l^32, l^48 (the four key quarters of a query column).
-__device__ __forceinline__ float quarter_max(float x) {
-  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = vmax3(__uint_as_float(p16[0]), __uint_as_float(p16[1]), __uint_as_float(p16[1]));
-  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return vmax3(__uint_as_float(p32[0]), __uint_as_float(p32[1]), __uint_as_float(p32[1]));
-}
 
 // Max / sum over lanes l, l^16, l^32, l^48 (the four key quarters of a query
 // column) with VALU lane swaps.
