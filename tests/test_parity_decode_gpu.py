@@ -122,6 +122,12 @@ DECODE_CASES = {
                     (0, 64)),
     "f32_d64_g8_bs32": (1, dict(batch=3, num_q_heads=16, num_kv_heads=2, block_size=32,
                                 ctx_fixed=(5, 64, 100), num_blocks=12, max_blocks_per_seq=4), (0, 32)),
+    # split units found by a scan with several sequences per lane (200 > 64)
+    "bf16_200_seqs": (2, dict(batch=200, num_q_heads=8, num_kv_heads=2, ctx_min=1, ctx_max=70,
+                              max_blocks_per_seq=5), (0, 16, 32)),
+    # more than 1024 sequences: the split kernel falls back to a (head, sequence, partition) grid
+    "bf16_1100_seqs": (2, dict(batch=1100, num_q_heads=8, num_kv_heads=2, ctx_min=1, ctx_max=40,
+                               max_blocks_per_seq=3), (16,)),
 }
 
 
