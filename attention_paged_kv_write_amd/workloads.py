@@ -284,6 +284,112 @@ def make_prefill_case(spec: PrefillSpec, seed: int) -> PrefillCase:
                        block_tables=tables, num_blocks=NB)
 
 
+# --------------------------------------------------------------------------
+# Paged (chunked / prefix-cached) prefill workloads
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PagedPrefillSpec:
+    name: str
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int = 16
+    prefix_min: int = 0           # cached positions before the chunk
+    prefix_max: int = 0
+    chunk_min: int = 1            # new query rows (their K/V are written first)
+    chunk_max: int = 1
+    prefix_fixed: Optional[tuple] = None
+    chunk_fixed: Optional[tuple] = None
+    pool_factor: float = 1.25
+
+
+@dataclass
+class PagedPrefillCase:
+    spec: PagedPrefillSpec
+    q: np.ndarray             # [T_q, H_q, d]
+    k_cache: np.ndarray       # [NB, H_kv, bs, d], the cached prefixes (NaN elsewhere)
+    v_cache: np.ndarray
+    k_new: np.ndarray         # [T_q, H_kv, d], the chunk's own K/V
+    v_new: np.ndarray
+    slot_mapping: np.ndarray  # [T_q] int32, where the chunk's K/V go
+    block_tables: np.ndarray  # [S, max_blocks] int32, -1 padded
+    context_lens: np.ndarray  # [S] int32 = prefix + chunk
+    cu_seqlens_q: np.ndarray  # [S+1] int32
+    scale: float
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_seqlen_q(self) -> int:
+        lens = np.diff(self.cu_seqlens_q)
+        return int(lens.max()) if lens.size else 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+
+def make_paged_prefill_case(spec: PagedPrefillSpec, seed: int) -> PagedPrefillCase:
+    """Draw order: prefix lengths, chunk lengths, block permutation, cached K/V
+    (iid over the whole pool, NaN where no prefix lives), chunk K/V, q."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, Hq, Hkv, d, bs = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads,
+                         spec.head_dim, spec.block_size)
+    if spec.prefix_fixed is not None:
+        pre = np.asarray(spec.prefix_fixed, dtype=np.int64)
+    else:
+        pre = rng.integers(spec.prefix_min, spec.prefix_max + 1, size=S).astype(np.int64)
+    if spec.chunk_fixed is not None:
+        chk = np.asarray(spec.chunk_fixed, dtype=np.int64)
+    else:
+        chk = rng.integers(spec.chunk_min, spec.chunk_max + 1, size=S).astype(np.int64)
+    assert pre.shape == (S,) and chk.shape == (S,)
+    ctx = pre + chk
+    nblk = (ctx + bs - 1) // bs
+    needed = int(nblk.sum())
+    NB = int(math.ceil(spec.pool_factor * needed)) if needed else 1
+    perm = rng.permutation(NB).astype(np.int32)
+    mbps = int(max(1, nblk.max() if nblk.size else 1))
+    tables = np.full((S, mbps), -1, dtype=np.int32)
+    c = 0
+    for s in range(S):
+        n = int(nblk[s])
+        tables[s, :n] = perm[c:c + n]
+        c += n
+    k_cache = _draw(rng, (NB, Hkv, bs, d), spec.dtype)
+    v_cache = _draw(rng, (NB, Hkv, bs, d), spec.dtype)
+    live = np.zeros((NB, bs), dtype=bool)
+    for s in range(S):
+        for p in range(int(pre[s])):
+            live[tables[s, p // bs], p % bs] = True
+    dead = ~live[:, None, :]   # broadcast over the KV heads
+    k_cache[np.broadcast_to(dead, (NB, Hkv, bs))] = nan_value(spec.dtype)
+    v_cache[np.broadcast_to(dead, (NB, Hkv, bs))] = nan_value(spec.dtype)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chk)
+    T = int(cu[-1])
+    slots = np.empty(T, dtype=np.int32)
+    for s in range(S):
+        for i in range(int(chk[s])):
+            p = int(pre[s]) + i
+            slots[cu[s] + i] = tables[s, p // bs] * bs + p % bs
+    k_new = _draw(rng, (T, Hkv, d), spec.dtype)
+    v_new = _draw(rng, (T, Hkv, d), spec.dtype)
+    q = _draw(rng, (T, Hq, d), spec.dtype)
+    return PagedPrefillCase(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new,
+                            v_new=v_new, slot_mapping=slots, block_tables=tables,
+                            context_lens=ctx.astype(np.int32), cu_seqlens_q=cu,
+                            scale=1.0 / math.sqrt(d))
+
+
 def empty_pool(num_blocks: int, num_kv_heads: int, block_size: int,
                head_dim: int, dtype: str) -> np.ndarray:
     """A pool whose every slot holds NaN (nothing written yet)."""
@@ -321,12 +427,20 @@ LONG_CONTEXT_SPLIT_DECODE = DecodeSpec(
     ctx_fixed=(131072,) * 4, num_blocks=40960, max_blocks_per_seq=8192,
     write_new_token=False, v_dist="uniform", partition_size=512)
 
+# Chunked prefill against a cached prefix (the first widening past the five):
+# Llama-3-8B heads, 16 sequences, 0..3072 cached positions, 128..1024 new rows.
+LLAMA3_8B_CHUNKED_PREFILL = PagedPrefillSpec(
+    name="llama3_8b_chunked_paged_prefill_bf16", dtype=BF16, num_seqs=16,
+    num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+    prefix_min=0, prefix_max=3072, chunk_min=128, chunk_max=1024)
+
 CONFIGS = {
     1: TINY_DECODE_F32,
     2: LLAMA3_8B_DECODE,
     3: LLAMA3_8B_PREFILL,
     4: LLAMA2_70B_PREFIX_DECODE,
     5: LONG_CONTEXT_SPLIT_DECODE,
+    6: LLAMA3_8B_CHUNKED_PREFILL,
 }
 
 
@@ -335,11 +449,13 @@ def seed_for(config_index: int) -> int:
 
 
 def make_case(config_index: int, seed: Optional[int] = None, **overrides):
-    """Build workload ``config_index`` (1..5), optionally shrunk by overrides."""
+    """Build workload ``config_index`` (1..6), optionally shrunk by overrides."""
     spec = CONFIGS[config_index]
     if overrides:
         spec = replace(spec, **overrides)
     s = seed_for(config_index) if seed is None else seed
     if isinstance(spec, PrefillSpec):
         return make_prefill_case(spec, s)
+    if isinstance(spec, PagedPrefillSpec):
+        return make_paged_prefill_case(spec, s)
     return make_decode_case(spec, s)

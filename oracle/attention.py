@@ -27,7 +27,10 @@ Readings of points the pages leave open:
   * a partition i covers positions [i*P, min((i+1)*P, ctx)); empty ones carry
     lse = -inf and weight 0 in the log-sum-exp merge;
   * prefill uses one cu_seqlens for q and k: row i of a sequence sees keys
-    0..i of the same sequence.
+    0..i of the same sequence;
+  * paged prefill (a chunk of Lq new rows against ctx cached positions, the
+    chunk's own K/V already written): the chunk is the last Lq positions,
+    so row i sees positions 0..ctx-Lq+i (the causal mask aligned to the end).
 
 Every function here has a pin in tests/test_oracle_pins.py (nothing is left
 parity-unpinned).
@@ -276,6 +279,51 @@ def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
             scores = scale * (Q @ K.T)                       # [L, L]
             future = np.triu(np.ones((L, L), dtype=bool), 1)  # key j > row i
             scores[future] = -np.inf
+            m = scores.max(axis=1, keepdims=True)
+            w = np.exp(scores - m)
+            z = w.sum(axis=1, keepdims=True)
+            out[a:e, h, :] = (w / z) @ V
+            lse[a:e, h] = (m + np.log(z))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# paged prefill: a new chunk of queries against a cached prefix plus itself
+# ---------------------------------------------------------------------------
+def paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
+                  block_size, scale, dtype, heads=None, seqs=None):
+    """Chunked / prefix-cached prefill: out [T_q, H_q, d], lse [T_q, H_q].
+
+    The varlen call takes separate cumulative lengths for queries and keys
+    with causal=True ("Llama 4 inference doubling ...", section 2.4), and the
+    engine reuses cached KV of earlier requests (prefix caching, same page,
+    section 4.2).  Here the keys of sequence s are its first context_lens[s]
+    cache positions, fetched through its block table (section 3.1 paging),
+    and its Lq = cu_seqlens_q[s+1] - cu_seqlens_q[s] query rows are the last
+    Lq of those positions (their own K/V already written): row i sits at
+    position ctx - Lq + i and sees keys 0 .. ctx - Lq + i.
+    """
+    T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    out = np.zeros((T, Hq, d))
+    lse = np.full((T, Hq), -math.inf)
+    S = len(cu_seqlens_q) - 1
+    for s in (range(S) if seqs is None else seqs):
+        a, e = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        Lq = e - a
+        ctx = int(context_lens[s])
+        if Lq <= 0:
+            continue
+        if Lq > ctx:
+            raise ValueError(f"sequence {s}: {Lq} query rows but only {ctx} cached positions")
+        for h in (range(Hq) if heads is None else heads):
+            g = group_of(h, Hq, Hkv)
+            K = upcast(gather(k_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0, :]
+            V = upcast(gather(v_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0, :]
+            Q = upcast(q[a:e, h, :], dtype)
+            scores = scale * (Q @ K.T)                                   # [Lq, ctx]
+            pos = ctx - Lq + np.arange(Lq)[:, None]                      # row positions
+            scores[np.arange(ctx)[None, :] > pos] = -np.inf
             m = scores.max(axis=1, keepdims=True)
             w = np.exp(scores - m)
             z = w.sum(axis=1, keepdims=True)

@@ -93,3 +93,28 @@ def write_slots(k_pool, v_pool, k_new, v_new, slots, block_size):
             kp[blk][h][off] = list(k_new[t][h])
             vp[blk][h][off] = list(v_new[t][h])
     return kp, vp
+
+
+def paged_prefill(q, k_pool, v_pool, tables, cu_q, ctx_lens, block_size, scale):
+    """q [T][Hq][d]; pools [NB][Hkv][bs][d]; row i of sequence s (Lq rows, ctx
+    keys) sees positions 0 .. ctx - Lq + i; returns out [T][Hq][d], lse [T][Hq]."""
+    T = len(q)
+    Hq = len(q[0])
+    Hkv = len(k_pool[0])
+    group = Hq // Hkv
+    out = [[None] * Hq for _ in range(T)]
+    lse = [[None] * Hq for _ in range(T)]
+    for s in range(len(cu_q) - 1):
+        start, end = cu_q[s], cu_q[s + 1]
+        lq = end - start
+        for i in range(lq):
+            last = ctx_lens[s] - lq + i
+            for h in range(Hq):
+                g = h // group
+                keys, values = [], []
+                for p in range(last + 1):
+                    blk = tables[s][p // block_size]
+                    keys.append(k_pool[blk][g][p % block_size])
+                    values.append(v_pool[blk][g][p % block_size])
+                out[start + i][h], lse[start + i][h] = softmax_attend(q[start + i][h], keys, values, scale)
+    return out, lse

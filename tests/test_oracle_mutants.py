@@ -84,6 +84,26 @@ def _prefill_mask(shift):
     return prefill
 
 
+def _paged_prefill_top_left(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
+                            block_size, scale, dtype, heads=None, seqs=None):
+    # mask aligned to the first cached position instead of the chunk's own
+    T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    out = np.zeros((T, Hq, d))
+    lse = np.full((T, Hq), -math.inf)
+    for s in range(len(cu_seqlens_q) - 1):
+        a, e = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        ctx = int(context_lens[s])
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            K = oa.upcast(oa.gather(k_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0]
+            V = oa.upcast(oa.gather(v_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0]
+            for i in range(e - a):
+                o, l, _ = oa.attend(oa.upcast(q[a + i, h], dtype), K[:i + 1], V[:i + 1], scale)
+                out[a + i, h], lse[a + i, h] = o, l
+    return out, lse
+
+
 def _reduce_counts_dead(part_out, part_lse, context_lens, partition_size):
     B, Hq, P, d = part_out.shape
     return oa.__dict__["_orig_reduce"](part_out, part_lse, np.full(B, P * partition_size), partition_size)
@@ -99,6 +119,7 @@ MUTANTS = {
     "causal_mask_hides_diagonal": [("prefill", _prefill_mask(0))],
     "causal_mask_leaks_next_key": [("prefill", _prefill_mask(2))],
     "merge_counts_dead_partitions": [("reduce_partitions", _reduce_counts_dead)],
+    "paged_prefill_mask_top_left": [("paged_prefill", _paged_prefill_top_left)],
 }
 
 PIN_CALLS = [
@@ -112,6 +133,7 @@ PIN_CALLS = [
     lambda g: pins.test_single_key_returns_its_value(),
     lambda g: pins.test_prefill_equals_dense_causal_sdpa(),
     lambda g: pins.test_split_then_merge_equals_unsplit(48),
+    lambda g: pins.test_paged_prefill_equals_masked_sdpa((7, 40, 100), (7, 13, 1), 16),
 ]
 
 

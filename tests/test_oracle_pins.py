@@ -444,6 +444,92 @@ def test_prefill_row0_is_v0_and_last_row_matches_decode():
 
 
 # ---------------------------------------------------------------------------
+# paged prefill (a chunk of queries against a cached prefix plus itself)
+# ---------------------------------------------------------------------------
+def _paged_prefill_inputs(rng, ctxs, chunks, Hq, Hkv, d, bs):
+    """Contiguous K/V per sequence paged into one shuffled pool, plus packed q."""
+    Ks = [rand_f32(rng, n, Hkv, d) for n in ctxs]
+    Vs = [rand_f32(rng, n, Hkv, d) for n in ctxs]
+    kp, vp, tables, ctx = paged_batch(Ks, Vs, bs, rng)
+    cu = np.zeros(len(chunks) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chunks)
+    q = rand_f32(rng, int(cu[-1]), Hq, d)
+    return Ks, Vs, kp, vp, tables, ctx, cu, q
+
+
+@pytest.mark.parametrize("ctxs,chunks,bs", [
+    ((7, 40, 100), (7, 13, 1), 16),
+    ((33, 64, 17), (5, 64, 16), 8),
+    ((1, 200), (1, 77), 32),
+])
+def test_paged_prefill_equals_masked_sdpa(ctxs, chunks, bs):
+    # torch SDPA on unpaged K/V with an explicit bottom-right causal mask
+    rng = np.random.default_rng(21)
+    Hq, Hkv, d = 8, 2, 32
+    Ks, Vs, kp, vp, tables, ctx, cu, q = _paged_prefill_inputs(rng, ctxs, chunks, Hq, Hkv, d, bs)
+    scale = 0.2
+    out, lse = oracle.paged_prefill(q, kp, vp, tables, cu, ctx, bs, scale, oracle.F32)
+    for s, (n, lq) in enumerate(zip(ctxs, chunks)):
+        a = int(cu[s])
+        Q = torch.from_numpy(q[a:a + lq].astype(np.float64)).permute(1, 0, 2)            # [Hq, lq, d]
+        K = torch.from_numpy(Ks[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        V = torch.from_numpy(Vs[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        allowed = torch.arange(n)[None, :] <= (n - lq + torch.arange(lq))[:, None]       # [lq, n]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q[None], K[None], V[None], attn_mask=allowed,
+                                                                scale=scale)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[a:a + lq], ref, rtol=0, atol=1e-12)
+        S = ((Q @ K.transpose(1, 2)) * scale).masked_fill(~allowed, float("-inf"))
+        np.testing.assert_allclose(lse[a:a + lq], torch.logsumexp(S, -1).T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_paged_prefill_special_cases():
+    rng = np.random.default_rng(22)
+    Hq, Hkv, d, bs = 4, 2, 16, 16
+    ctxs = (1, 20, 48)
+    # a chunk that is the whole sequence is the plain causal prefill of it
+    Ks, Vs, kp, vp, tables, ctx, cu, q = _paged_prefill_inputs(rng, ctxs, ctxs, Hq, Hkv, d, bs)
+    out, lse = oracle.paged_prefill(q, kp, vp, tables, cu, ctx, bs, 0.25, oracle.F32)
+    pout, plse = oracle.prefill(q, np.concatenate(Ks), np.concatenate(Vs), cu, 0.25, oracle.F32)
+    np.testing.assert_allclose(out, pout, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, plse, rtol=0, atol=1e-12)
+    # a one-row chunk is a decode of that row over the whole cache
+    cu1 = np.arange(len(ctxs) + 1, dtype=np.int32)
+    q1 = rand_f32(rng, len(ctxs), Hq, d)
+    out1, lse1 = oracle.paged_prefill(q1, kp, vp, tables, cu1, ctx, bs, 0.25, oracle.F32)
+    dout, dlse = oracle.decode(q1, kp, vp, tables, ctx, bs, 0.25, oracle.F32)
+    np.testing.assert_allclose(out1, dout, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse1, dlse, rtol=0, atol=1e-12)
+    # more rows than cached positions is an error
+    with pytest.raises(ValueError):
+        oracle.paged_prefill(q[:3], kp, vp, tables, np.array([0, 2, 2, 3], np.int32),
+                             np.array([1, 20, 48], np.int32), bs, 0.25, oracle.F32)
+
+
+def test_paged_prefill_brute_force_and_permutation():
+    case = wl.make_case(6, num_seqs=3, prefix_fixed=(0, 5, 21), chunk_fixed=(3, 1, 11),
+                        num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=8)
+    dt = case.spec.dtype
+    kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, 8)
+    out, lse = oracle.paged_prefill(case.q, kc, vc, case.block_tables, case.cu_seqlens_q,
+                                    case.context_lens, 8, case.scale, dt)
+    up = lambda x: oracle.upcast(x, dt).tolist()
+    bout, blse = brute.paged_prefill(up(case.q), up(kc), up(vc), case.block_tables.tolist(),
+                                     case.cu_seqlens_q.tolist(), case.context_lens.tolist(), 8, case.scale)
+    np.testing.assert_allclose(out, np.array(bout), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(blse), rtol=0, atol=1e-12)
+    # moving every physical block elsewhere (tables follow) changes nothing
+    perm = np.random.default_rng(5).permutation(kc.shape[0])
+    kp = np.empty_like(kc)
+    vp = np.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc
+    tables = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1).astype(np.int32)
+    out2, lse2 = oracle.paged_prefill(case.q, kp, vp, tables, case.cu_seqlens_q, case.context_lens, 8,
+                                      case.scale, dt)
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(lse2, lse)
+
+
+# ---------------------------------------------------------------------------
 # the generator itself
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,over", [
