@@ -214,10 +214,70 @@ int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k, c
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.scale_log2 = scale * pa::kLog2e;
+  a.block_tables = nullptr;
+  a.context_lens = nullptr;
+  a.block_size = 0;
+  a.max_blocks_per_seq = 0;
+  a.num_blocks = 0;
+  a.max_context_len = 0;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_prefill_generic(a, dt, head_dim, s)
                                            : pa::launch_prefill(a, dt, head_dim, s);
+  return launch_status(e, fn);
+}
+
+int paged_prefill(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                  int num_seqs, int total_q, int max_seqlen_q, int num_q_heads, int num_kv_heads,
+                  int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                  int max_context_len, float scale, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_prefill";
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
+  if (max_seqlen_q > total_q) return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen_q > total_q", fn);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+  if (!(block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  if (!group_ok(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, num_q_heads / num_kv_heads);
+  if (static_cast<int64_t>(num_q_heads) * num_seqs > INT32_MAX || num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%s: too many sequences", fn);
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!out || !lse || !q || !k_cache || !v_cache || !block_tables || !cu_seqlens_q || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::PrefillArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.cu_seqlens = cu_seqlens_q;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_q;
+  a.max_seqlen = max_seqlen_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * pa::kLog2e;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = g_force_vector_path ? pa::launch_paged_prefill_generic(a, dt, head_dim, s)
+                                           : pa::launch_paged_prefill(a, dt, head_dim, s);
   return launch_status(e, fn);
 }
 

@@ -61,15 +61,22 @@ struct PrefillArgs {
   void* out;             // [T, H_q, d]
   float* lse;            // [T, H_q]
   const void* q;         // [T, H_q, d]
-  const void* k;         // [T, H_kv, d]
+  const void* k;         // varlen: [T, H_kv, d]; paged: k_cache [NB, H_kv, bs, d]
   const void* v;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens;   // query rows (and varlen keys) per sequence, [S+1]
   int num_seqs;
-  int total_tokens;
-  int max_seqlen;
+  int total_tokens;      // query rows
+  int max_seqlen;        // longest query run
   int num_q_heads;
   int num_kv_heads;
   float scale_log2;
+  // paged prefill only (block_tables == nullptr for the varlen call)
+  const int32_t* block_tables;  // [S, max_blocks_per_seq]
+  const int32_t* context_lens;  // [S] cached positions, the chunk included
+  int block_size;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int max_context_len;
 };
 
 enum class DType { F32 = 0, BF16 = 1 };
@@ -84,5 +91,8 @@ hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStrea
 // The vector-ALU kernels alone (also the path for shapes without an MFMA kernel).
 hipError_t launch_decode_generic(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
+// Paged prefill: the same kernels with keys read through the block table.
+hipError_t launch_paged_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
+hipError_t launch_paged_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -58,6 +58,27 @@ __device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int s) {
   return SeqSpan{lo, min(hi - lo, a.max_seqlen)};
 }
 
+// Keys of sequence s: positions 0 .. ctx-1, the first query row at position
+// pos0 (so row r sees keys 0 .. pos0 + r).  Varlen: the sequence's own rows,
+// pos0 = 0.  Paged: its cached positions (capped at what the table and
+// max_context_len allow), the chunk being the last len of them; ctx < len is
+// a precondition violation, reported as ctx = 0 (the rows are skipped).
+struct KeySpan {
+  int ctx, pos0;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ KeySpan key_span(const PrefillArgs& a, int s, int len) {
+  if constexpr (!PAGED) {
+    return KeySpan{len, 0};
+  } else {
+    const int cap = min(a.max_context_len, a.max_blocks_per_seq * a.block_size);
+    const int ctx = clampi(a.context_lens[s], 0, cap);
+    if (ctx < len) return KeySpan{0, 0};
+    return KeySpan{ctx, ctx - len};
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -82,7 +103,7 @@ __device__ __forceinline__ float quarter_reduce(float x, Op op) {
 // Four waves per workgroup: NW query heads of one KV group times 4/NW row
 // blocks; each wave owns 32 query rows (two 16-row groups) of one head, so a
 // K/V fragment read from LDS feeds two MFMAs.
-template <int NW>
+template <int NW, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int ntiles) {
   constexpr int NR = 4 / NW;
   constexpr int PM = 32 * NR;   // query rows per workgroup
@@ -112,6 +133,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int qt = (sp.len + PM - 1) / PM - 1 - w;
   if (qt < 0) return;
   const int qw0 = qt * PM;   // the workgroup's first row
+  const KeySpan ks = key_span<PAGED>(a, s, sp.len);
+  if (ks.ctx == 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
@@ -131,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   bf16x8 qf[RG][4];   // Q^T B operands, loaded below (after the first tile is requested)
-  const int kend = min(qw0 + PM, sp.len);   // keys 0 .. kend-1 are needed by the workgroup
+  const int kend = min(ks.pos0 + qw0 + PM, ks.ctx);   // keys 0 .. kend-1 are needed by the workgroup
   const int nkt = (kend + kPN - 1) / kPN;
 
   // LDS-DMA of key tile kt: 2048 chunks (K then V); wave w issues slices
@@ -143,12 +166,30 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int drow = 4 * wave + j;   // row of slice `wave`; later slices add 16
   const int kchunk = c16 ^ (drow & 15);
   const int vchunk = c16 ^ (2 * (drow & 7));
+  // Paged: the physical blocks of this lane's four rows of a tile, loaded one
+  // tile ahead of its DMA (ids_next) so the table read never delays it.
+  const int32_t* table = PAGED ? a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq : nullptr;
+  const int lbs = PAGED ? __builtin_ctz(a.block_size) : 0;
+  int ids_cur[4] = {0, 0, 0, 0}, ids_next[4] = {0, 0, 0, 0};
+  auto load_ids = [&](int kt, int (&ids)[4]) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) ids[mm] = table[min(kt * kPN + drow + 16 * mm, ks.ctx - 1) >> lbs];
+    }
+  };
   auto issue = [&](int kt, u32x4* buf) {
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
       const int row = drow + 16 * (ii & 3);
-      const int key = min(kt * kPN + row, sp.len - 1);
-      const size_t rowoff = (static_cast<size_t>(sp.start + key) * Hkv + g) * RC;
+      const int key = min(kt * kPN + row, ks.ctx - 1);
+      size_t rowoff;
+      if constexpr (PAGED) {
+        int phys = ids_cur[ii & 3];
+        phys = (phys >= 0 && phys < a.num_blocks) ? phys : 0;   // bad ids read block 0 (result unspecified)
+        rowoff = ((static_cast<size_t>(phys) * Hkv + g) * a.block_size + (key & (a.block_size - 1))) * RC;
+      } else {
+        rowoff = (static_cast<size_t>(sp.start + key) * Hkv + g) * RC;
+      }
       const u32x4* src = ii < 4 ? kc + rowoff + kchunk : vc + rowoff + vchunk;
       global_to_lds16(src, &buf[64 * (wave + 4 * ii)]);
     }
@@ -198,25 +239,26 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     bf16x8 pf[2][RG];   // P^T B operands: [key chunk of 32][rg]
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      if (masked) {
-        const int qrow = q0 + 16 * rg + c16;
+      // scaled scores (log2 units).  The multiply also hands the matrix-core
+      // results to the vector ALU under the compiler's hazard tracking before
+      // the inline-asm max reads them.
+      float sv[4][4];
+      const int qrow = ks.pos0 + q0 + 16 * rg + c16;   // the row's position among the keys
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kt * kPN + 16 * nt + 4 * j + i > qrow) sacc[nt][rg][i] = kNegInf;
-      }
-      // row max of the raw scores
-      float mx = vmax3(vmax3(sacc[0][rg][0], sacc[0][rg][1], sacc[0][rg][2]),
-                       vmax3(sacc[0][rg][3], sacc[1][rg][0], sacc[1][rg][1]),
-                       vmax3(sacc[1][rg][2], sacc[1][rg][3], sacc[2][rg][0]));
-      mx = vmax3(mx, vmax3(sacc[2][rg][1], sacc[2][rg][2], sacc[2][rg][3]),
-                 vmax3(sacc[3][rg][0], sacc[3][rg][1], vmax3(sacc[3][rg][2], sacc[3][rg][3], sacc[3][rg][3])));
-      mx = quarter_max(mx) * sl2;
+        for (int i = 0; i < 4; ++i) {
+          sv[nt][i] = sacc[nt][rg][i] * sl2;
+          if (masked && kt * kPN + 16 * nt + 4 * j + i > qrow) sv[nt][i] = kNegInf;
+        }
+      float mx = vmax3(vmax3(sv[0][0], sv[0][1], sv[0][2]), vmax3(sv[0][3], sv[1][0], sv[1][1]),
+                       vmax3(sv[1][2], sv[1][3], sv[2][0]));
+      mx = vmax3(mx, vmax3(sv[2][1], sv[2][2], sv[2][3]), vmax3(sv[3][0], sv[3][1], vmax3(sv[3][2], sv[3][3], sv[3][3])));
+      mx = quarter_max(mx);
       // lazy rescale: the whole wave moves its maxima only when some row's
-      // max has grown past the slack.  Every processed tile holds at least one
-      // visible key of every row, so mx is finite and the first tile always
-      // moves m off -inf (alpha = 0 then).
+      // max has grown past the slack.  The first tile holds key 0, visible to
+      // every row, so m leaves -inf there (alpha = 0); a row with no visible
+      // key in a later masked tile has mx = -inf and keeps its m.
       const uint64_t grow = __builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack);
       if (grow) {
         const float m_new = fmaxf(m[rg], mx);
@@ -226,18 +268,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
         for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
       }
-      const float nm = -m[rg];
       uint32_t pw[4][2];
       float ps[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float t = fmaf(sacc[nt][rg][i], sl2, nm);
-          if (masked) t = sacc[nt][rg][i] == kNegInf ? kNegInf : t;
-          pv[i] = fast_exp2(t);
-        }
+        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[nt][i] - m[rg]);   // masked: exp2(-inf) = 0
         ps[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
         pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
@@ -268,11 +305,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 
   // Double-buffered: the DMA of tile kt+1 runs while tile kt is computed.  A
   // buffer is refilled only after the barrier that follows its last reads.
-  // The wave's 32 rows (q0 is a multiple of 32) meet the diagonal in key tile
-  // q0/64 alone: earlier tiles need no mask, later ones are skipped (every
+  // The wave's rows sit at key positions P0 .. P0 + 31 (P0 = pos0 + q0): key
+  // tiles below (P0 + 1) / 64 are wholly visible, those up to the last live
+  // row's position need the causal mask (one tile when pos0 = 0, since q0 is
+  // a multiple of 32; at most two otherwise), later ones are skipped (every
   // wave still joins each barrier).
-  const int kt_diag = sp.len > q0 ? q0 / kPN : -1;   // -1: all rows are padding
+  const bool wave_live = sp.len > q0;   // else every row of the wave is padding
+  const int n_full = wave_live ? (ks.pos0 + q0 + 1) >> 6 : 0;
+  const int kt_last = wave_live ? (ks.pos0 + min(q0 + 31, sp.len - 1)) >> 6 : -1;
+  load_ids(0, ids_cur);
   issue(0, kvbuf);   // the first tile's loads overlap the Q loads
+  if (nkt > 1) load_ids(1, ids_next);
 
   // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.  Rows past
   // the sequence load its last row (all eight loads in flight at once) and are
@@ -297,9 +340,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   for (int kt = 0; kt < nkt; ++kt) {
     wait_dma_all();
     __syncthreads();
-    if (kt + 1 < nkt) issue(kt + 1, kvbuf + ((kt + 1) & 1) * 2048);
-    if (kt < kt_diag) tile(kt, false);
-    else if (kt == kt_diag) tile(kt, true);
+    if (kt + 1 < nkt) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) ids_cur[mm] = ids_next[mm];
+      issue(kt + 1, kvbuf + ((kt + 1) & 1) * 2048);
+      if (kt + 2 < nkt) load_ids(kt + 2, ids_next);
+    }
+    if (kt < n_full) tile(kt, false);
+    else if (kt <= kt_last) tile(kt, true);
   }
 
   uint16_t* out = static_cast<uint16_t*>(a.out);
@@ -325,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 // ---------------------------------------------------------------------------
 // Vector-ALU kernel: 4 query rows per workgroup, one per wave.
 // ---------------------------------------------------------------------------
-template <bool BF, int D>
+template <bool BF, int D, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int group) {
   constexpr int ESZ = BF ? 2 : 4;
   constexpr int VEC = 16 / ESZ;
@@ -338,6 +386,10 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int
   const SeqSpan sp = seq_span(a, s);
   const int i = blockIdx.x * 4 + wave;
   if (i >= sp.len) return;
+  const KeySpan ks = key_span<PAGED>(a, s, sp.len);
+  if (ks.ctx == 0) return;
+  const int last = ks.pos0 + i;   // the row sees keys 0 .. last
+  const int32_t* table = PAGED ? a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq : nullptr;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int g = h / group;
   const int rg = lane / LPT, dl = lane % LPT;
@@ -351,12 +403,19 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  for (int k0 = 0; k0 <= i; k0 += TPW) {
+  for (int k0 = 0; k0 <= last; k0 += TPW) {
     const int key = k0 + rg;
-    const bool valid = key <= i;
+    const bool valid = key <= last;
     float kf[VEC], vf[VEC];
     if (valid) {
-      const size_t rb = (static_cast<size_t>(sp.start + key) * Hkv + g) * RC + dl;
+      size_t rb;
+      if constexpr (PAGED) {
+        int phys = table[key / a.block_size];
+        phys = (phys >= 0 && phys < a.num_blocks) ? phys : 0;
+        rb = ((static_cast<size_t>(phys) * Hkv + g) * a.block_size + key % a.block_size) * RC + dl;
+      } else {
+        rb = (static_cast<size_t>(sp.start + key) * Hkv + g) * RC + dl;
+      }
       unpack16<BF>(kc[rb], kf);
       unpack16<BF>(vc[rb], vf);
     } else {
@@ -405,42 +464,63 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int
   if (dl == 0) a.lse[orow] = (m + __log2f(l)) * kLn2;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
-  if (a.num_seqs == 0 || a.max_seqlen == 0) return hipSuccess;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  if (dt == DType::BF16 && head_dim == kD) {
-    const int nw = group >= 4 ? 4 : group;   // heads of one KV group per workgroup
-    const int pm = 32 * (4 / nw);            // query rows per workgroup
-    const int ntiles = (a.max_seqlen + pm - 1) / pm;
-    const int ncol = a.num_kv_heads * (group / nw);
-    const int64_t n = 8LL * ((ncol + 7) / 8) * a.num_seqs * ntiles;
-    if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
-    const dim3 grid(static_cast<unsigned>(n));
-    switch (nw) {
-      case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4>), grid, dim3(256), 0, s, a, group, ntiles); break;
-      case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2>), grid, dim3(256), 0, s, a, group, ntiles); break;
-      default: hipLaunchKernelGGL((prefill_mfma_kernel<1>), grid, dim3(256), 0, s, a, group, ntiles); break;
-    }
-    return hipGetLastError();
+namespace {
+
+template <bool PAGED>
+hipError_t launch_mfma(const PrefillArgs& a, int group, hipStream_t s) {
+  const int nw = group >= 4 ? 4 : group;   // heads of one KV group per workgroup
+  const int pm = 32 * (4 / nw);            // query rows per workgroup
+  const int ntiles = (a.max_seqlen + pm - 1) / pm;
+  const int ncol = a.num_kv_heads * (group / nw);
+  const int64_t n = 8LL * ((ncol + 7) / 8) * a.num_seqs * ntiles;
+  if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
+  const dim3 grid(static_cast<unsigned>(n));
+  switch (nw) {
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
+    default: hipLaunchKernelGGL((prefill_mfma_kernel<1, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
   }
-  return launch_prefill_generic(a, dt, head_dim, s);
+  return hipGetLastError();
 }
 
-hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
+template <bool PAGED>
+hipError_t launch_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
   if (a.num_seqs == 0 || a.max_seqlen == 0) return hipSuccess;
   const int group = a.num_q_heads / a.num_kv_heads;
   const dim3 grid(static_cast<unsigned>((a.max_seqlen + 3) / 4), static_cast<unsigned>(a.num_q_heads),
                   static_cast<unsigned>(a.num_seqs));
   if (dt == DType::BF16) {
-    if (head_dim == 64) hipLaunchKernelGGL((prefill_generic_kernel<true, 64>), grid, dim3(256), 0, s, a, group);
-    else if (head_dim == 128) hipLaunchKernelGGL((prefill_generic_kernel<true, 128>), grid, dim3(256), 0, s, a, group);
+    if (head_dim == 64) hipLaunchKernelGGL((prefill_generic_kernel<true, 64, PAGED>), grid, dim3(256), 0, s, a, group);
+    else if (head_dim == 128) hipLaunchKernelGGL((prefill_generic_kernel<true, 128, PAGED>), grid, dim3(256), 0, s, a, group);
     else return hipErrorNotSupported;
   } else {
-    if (head_dim == 64) hipLaunchKernelGGL((prefill_generic_kernel<false, 64>), grid, dim3(256), 0, s, a, group);
-    else if (head_dim == 128) hipLaunchKernelGGL((prefill_generic_kernel<false, 128>), grid, dim3(256), 0, s, a, group);
+    if (head_dim == 64) hipLaunchKernelGGL((prefill_generic_kernel<false, 64, PAGED>), grid, dim3(256), 0, s, a, group);
+    else if (head_dim == 128) hipLaunchKernelGGL((prefill_generic_kernel<false, 128, PAGED>), grid, dim3(256), 0, s, a, group);
     else return hipErrorNotSupported;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
+  if (a.num_seqs == 0 || a.max_seqlen == 0) return hipSuccess;
+  if (dt == DType::BF16 && head_dim == kD) return launch_mfma<false>(a, a.num_q_heads / a.num_kv_heads, s);
+  return launch_generic<false>(a, dt, head_dim, s);
+}
+
+hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
+  return launch_generic<false>(a, dt, head_dim, s);
+}
+
+hipError_t launch_paged_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
+  if (a.num_seqs == 0 || a.max_seqlen == 0) return hipSuccess;
+  if (dt == DType::BF16 && head_dim == kD) return launch_mfma<true>(a, a.num_q_heads / a.num_kv_heads, s);
+  return launch_generic<true>(a, dt, head_dim, s);
+}
+
+hipError_t launch_paged_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t s) {
+  return launch_generic<true>(a, dt, head_dim, s);
 }
 
 }  // namespace pa

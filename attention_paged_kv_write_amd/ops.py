@@ -24,6 +24,7 @@ PA_OPT_FORCE_VECTOR_PATH = 1
 EXPORTED_SYMBOLS = (
     "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
+    "paged_prefill",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -63,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.varlen_causal_prefill.restype = i32
     lib.varlen_causal_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           f32, i32, vp]
+    lib.paged_prefill.restype = i32
+    lib.paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, i32, f32, i32, vp]
     _lib = lib
     return lib
 
@@ -230,4 +234,38 @@ def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                      _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
                                      cu_seqlens.shape[0] - 1, T, int(max_seqlen), Hq, Hkv, d,
                                      float(scale), dt, _stream(q)))
+    return out, lse
+
+
+def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor, context_lens: torch.Tensor,
+                  max_seqlen_q: int, max_context_len: int, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """A chunk of query rows per sequence (the last rows of its cache) against its
+    paged cache -> (out [T_q,H_q,d], lse [T_q,H_q])."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    T, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("paged_prefill: inconsistent q / cache shapes or dtypes")
+    S = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_q.dim() != 1 or S < 0 or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or context_lens.shape != (S,):
+        raise ValueError("paged_prefill: cu_seqlens_q / block_tables / context_lens shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.paged_prefill(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
+                             _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+                             _dev(v_cache, "v_cache", ndim=4),
+                             _dev(block_tables, "block_tables", torch.int32, 2),
+                             _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1),
+                             _dev(context_lens, "context_lens", torch.int32, 1),
+                             S, T, int(max_seqlen_q), Hq, Hkv, d, bs, block_tables.shape[1], NB,
+                             int(max_context_len), float(scale), dt, _stream(q)))
     return out, lse

@@ -6,6 +6,8 @@
  *   paged_attention_decode  one query token per sequence against its paged history
  *   paged_attention_reduce  log-sum-exp merge of split-KV partitions
  *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
+ * and a fifth extends prefill to a cached prefix:
+ *   paged_prefill           a chunk of query rows against its sequence's paged cache
  *
  * Conventions shared by every call
  * --------------------------------
@@ -187,6 +189,39 @@ int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k,
                           int total_tokens, int max_seqlen, int num_q_heads,
                           int num_kv_heads, int head_dim, float scale, pa_dtype dtype,
                           void* stream);
+
+/*
+ * paged_prefill - a chunk of new query rows per sequence against its paged cache.
+ *
+ * The varlen call of "Llama 4 inference doubling (FlashAttention-3 + PagedAttention +
+ * vLLM)" takes separate cumulative lengths for queries and keys (section 2.4), and the
+ * engine reuses cached KV of earlier requests (prefix caching, section 4.2).  Here the
+ * keys of sequence s are its first ctx = context_lens[s] cached positions, read through
+ * its block table as in paged_attention_decode, and its Lq = cu_seqlens_q[s+1] -
+ * cu_seqlens_q[s] query rows are the LAST Lq of those positions (their own K/V already
+ * written, e.g. by paged_kv_write): row i (token t = cu_seqlens_q[s] + i) sits at
+ * position ctx - Lq + i and attends, for query head h, to positions 0 .. ctx - Lq + i
+ * of KV head h / G (the causal mask aligned to the end of the cache).  With ctx = Lq
+ * this is varlen_causal_prefill over the pool; with Lq = 1 it is a decode.
+ *   out[t, h, :], lse[t, h] as in varlen_causal_prefill
+ *   q, out        [total_q, H_q, head_dim], dtype; lse float32 [total_q, H_q]
+ *   k_cache, v_cache, block_tables, block_size, max_blocks_per_seq, num_blocks,
+ *                 max_context_len: as in paged_attention_decode
+ *   cu_seqlens_q  int32 [num_seqs + 1], within [0, total_q]
+ *   context_lens  int32 [num_seqs]; must be >= the sequence's query rows (a sequence
+ *                 violating this has its rows left unwritten)
+ *   max_seqlen_q  host-side upper bound on any sequence's query rows (sizes the grid)
+ * Query rows not covered by any sequence are not written.
+ * Supported: dtype bf16, head_dim 128 (MFMA path); dtype f32 or bf16 with head_dim 64
+ *   or 128 (vector path); block_size 8, 16, 32 or 64; H_q / H_kv in {1, 2, 4, 8};
+ *   num_seqs <= 65535; max_seqlen_q <= total_q.
+ */
+int paged_prefill(void* out, float* lse, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* block_tables,
+                  const int32_t* cu_seqlens_q, const int32_t* context_lens, int num_seqs,
+                  int total_q, int max_seqlen_q, int num_q_heads, int num_kv_heads,
+                  int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                  int max_context_len, float scale, pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

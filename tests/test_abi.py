@@ -29,10 +29,10 @@ def lib():
     return ops.load_library()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("paged_kv_write", "paged_attention_decode", "paged_attention_reduce",
-              "varlen_causal_prefill"):
+              "varlen_causal_prefill", "paged_prefill"):
         assert n in names
     assert set(names) == set(ops.EXPORTED_SYMBOLS)
 
@@ -110,6 +110,29 @@ def test_prefill_validation(lib):
     assert f(p, p, p, p, p, p, 2, 100, 60, 32, 8, 72, 0.1, 1, None) == 2      # head_dim
     assert f(None, None, None, None, None, None, 2, 100, 60, 32, 8, 128, 0.1, 1, None) == 1
     assert f(p, p, p, p, p, p, 0, 100, 60, 32, 8, 128, 0.1, 1, None) == 0
+
+
+def test_paged_prefill_validation(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.paged_prefill
+    # (out, lse, q, kc, vc, tables, cu_q, ctx, S, T, max_q, Hq, Hkv, d, bs, mbps, NB, maxctx, scale, dt, stream)
+    ok = dict(S=2, T=100, mq=60, Hq=32, Hkv=8, d=128, bs=16, mbps=8, NB=20, mc=128, scale=0.1, dt=1)
+
+    def call(ptr=p, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, a["S"], a["T"], a["mq"], a["Hq"], a["Hkv"], a["d"],
+                 a["bs"], a["mbps"], a["NB"], a["mc"], a["scale"], a["dt"], None)
+    assert call(Hkv=6) == 1                      # 32 % 6
+    assert call(mq=101) == 1                     # max_seqlen_q > total_q
+    assert call(mc=129) == 1                     # max_context_len > mbps * bs
+    assert call(scale=float("inf")) == 1
+    assert call(d=72) == 2                       # head_dim
+    assert call(bs=24) == 2                      # block_size
+    assert call(Hq=48, Hkv=3) == 2               # group 16
+    assert call(ptr=None) == 1                   # null pointers
+    assert call(S=0) == 0                        # nothing to do
+    assert call(T=0, mq=0) == 0
 
 
 def test_option(lib):
