@@ -6,4 +6,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 from .attention import (  # noqa: F401
     BF16, F32, attend, decode, decode_one, decode_partitions, gather,
     group_of, kv_write, num_partitions, paged_prefill, prefill, reduce_partitions, upcast,
+    window_start,
 )

@@ -30,7 +30,10 @@ Readings of points the pages leave open:
     0..i of the same sequence;
   * paged prefill (a chunk of Lq new rows against ctx cached positions, the
     chunk's own K/V already written): the chunk is the last Lq positions,
-    so row i sees positions 0..ctx-Lq+i (the causal mask aligned to the end).
+    so row i sees positions 0..ctx-Lq+i (the causal mask aligned to the end);
+  * a sliding window of W keys (0 = none) keeps positions max(0, p-W+1)..p
+    for a query at position p; a split partition wholly before the window is
+    empty (out 0, lse -inf).
 
 Every function here has a pin in tests/test_oracle_pins.py (nothing is left
 parity-unpinned).
@@ -156,14 +159,22 @@ def decode_one(q, k_cache, v_cache, block_tables, context_lens, block_size,
     return attend(upcast(q[b, h], dtype), K, V, scale)
 
 
+def window_start(pos, window):
+    """First key a query at position pos sees under a sliding window of
+    `window` keys (0 = no window): max(0, pos - window + 1), the row mask of
+    "PageAttention + FlashAttention golden combination", section 4.1."""
+    return max(0, int(pos) - int(window) + 1) if window > 0 else 0
+
+
 def decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
-           dtype, return_probs=False):
+           dtype, return_probs=False, window=0):
     """PagedAttention decode for a batch: out [B, H_q, d] float64, lse [B, H_q].
 
     Each new token attends over its sequence's whole history, gathered block
     by block through the table ("PageAttention + FlashAttention golden
     combination", section 2.1; LLaMA page, section 3.2), with query heads
-    sharing KV heads in groups (LLaMA page, section 2.1).
+    sharing KV heads in groups (LLaMA page, section 2.1).  With a sliding
+    window only the last `window` positions are seen.
     """
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
@@ -172,8 +183,9 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
     probs = {}
     for b in range(B):
         ctx = int(context_lens[b])
-        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)
-        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)
+        lo = window_start(ctx - 1, window) if ctx > 0 else 0
+        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)[lo:]
+        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)[lo:]
         for h in range(Hq):
             g = group_of(h, Hq, Hkv)
             o, l, p = attend(upcast(q[b, h], dtype), Kall[:, g, :], Vall[:, g, :], scale)
@@ -193,11 +205,12 @@ def num_partitions(max_context_len, partition_size):
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
                       block_size, scale, dtype, partition_size,
-                      max_partitions=None):
+                      max_partitions=None, window=0):
     """Attention restricted to each partition of positions.
 
     Returns part_out [B, H_q, P, d] and part_lse [B, H_q, P]; a partition that
-    holds no position of the sequence has out 0 and lse -inf.
+    holds no visible position of the sequence (past its end, or wholly before
+    a sliding window) has out 0 and lse -inf.
     """
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
@@ -208,8 +221,9 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
         ctx = int(context_lens[b])
         Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)
         Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)
+        wlo = window_start(ctx - 1, window) if ctx > 0 else 0
         for i in range(P):
-            lo, hi = i * partition_size, min((i + 1) * partition_size, ctx)
+            lo, hi = max(i * partition_size, wlo), min((i + 1) * partition_size, ctx)
             if lo >= hi:
                 continue
             for h in range(Hq):
@@ -251,7 +265,7 @@ def reduce_partitions(part_out, part_lse, context_lens, partition_size):
 # ---------------------------------------------------------------------------
 # varlen causal prefill
 # ---------------------------------------------------------------------------
-def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
+def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None, window=0):
     """Causal self-attention of each packed sequence: out [T, H_q, d], lse [T, H_q].
 
     Sequences are packed back to back and delimited by the cumulative length
@@ -259,7 +273,9 @@ def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
     the varlen call with causal=True returning out and lse).  Within sequence
     s, row i sees keys 0..i of the same sequence: the causal mask of the
     LLaMA page's section 3.1 step 4, built with -inf so masked keys get
-    weight 0.  ``heads``/``seqs`` restrict the computation to a subset.
+    weight 0.  With a sliding window row i also loses keys before
+    i - window + 1 ("PageAttention + FlashAttention golden combination",
+    section 4.1).  ``heads``/``seqs`` restrict the computation to a subset.
     """
     T, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -279,6 +295,8 @@ def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
             scores = scale * (Q @ K.T)                       # [L, L]
             future = np.triu(np.ones((L, L), dtype=bool), 1)  # key j > row i
             scores[future] = -np.inf
+            if window > 0:
+                scores[np.tril(np.ones((L, L), dtype=bool), -window)] = -np.inf  # key j <= i - window
             m = scores.max(axis=1, keepdims=True)
             w = np.exp(scores - m)
             z = w.sum(axis=1, keepdims=True)
@@ -291,7 +309,7 @@ def prefill(q, k, v, cu_seqlens, scale, dtype, heads=None, seqs=None):
 # paged prefill: a new chunk of queries against a cached prefix plus itself
 # ---------------------------------------------------------------------------
 def paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
-                  block_size, scale, dtype, heads=None, seqs=None):
+                  block_size, scale, dtype, heads=None, seqs=None, window=0):
     """Chunked / prefix-cached prefill: out [T_q, H_q, d], lse [T_q, H_q].
 
     The varlen call takes separate cumulative lengths for queries and keys
@@ -301,7 +319,8 @@ def paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
     cache positions, fetched through its block table (section 3.1 paging),
     and its Lq = cu_seqlens_q[s+1] - cu_seqlens_q[s] query rows are the last
     Lq of those positions (their own K/V already written): row i sits at
-    position ctx - Lq + i and sees keys 0 .. ctx - Lq + i.
+    position ctx - Lq + i and sees keys 0 .. ctx - Lq + i (with a sliding
+    window, only the last `window` of those).
     """
     T, Hq, d = q.shape
     Hkv = k_cache.shape[1]
@@ -324,6 +343,8 @@ def paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
             scores = scale * (Q @ K.T)                                   # [Lq, ctx]
             pos = ctx - Lq + np.arange(Lq)[:, None]                      # row positions
             scores[np.arange(ctx)[None, :] > pos] = -np.inf
+            if window > 0:
+                scores[np.arange(ctx)[None, :] <= pos - window] = -np.inf
             m = scores.max(axis=1, keepdims=True)
             w = np.exp(scores - m)
             z = w.sum(axis=1, keepdims=True)

@@ -104,6 +104,10 @@ def _paged_prefill_top_left(q, k_cache, v_cache, block_tables, cu_seqlens_q, con
     return out, lse
 
 
+def _window_start_off_by_one(pos, window):
+    return max(0, int(pos) - int(window)) if window > 0 else 0
+
+
 def _reduce_counts_dead(part_out, part_lse, context_lens, partition_size):
     B, Hq, P, d = part_out.shape
     return oa.__dict__["_orig_reduce"](part_out, part_lse, np.full(B, P * partition_size), partition_size)
@@ -120,6 +124,7 @@ MUTANTS = {
     "causal_mask_leaks_next_key": [("prefill", _prefill_mask(2))],
     "merge_counts_dead_partitions": [("reduce_partitions", _reduce_counts_dead)],
     "paged_prefill_mask_top_left": [("paged_prefill", _paged_prefill_top_left)],
+    "window_one_key_too_many": [("window_start", _window_start_off_by_one)],
 }
 
 PIN_CALLS = [
@@ -134,6 +139,7 @@ PIN_CALLS = [
     lambda g: pins.test_prefill_equals_dense_causal_sdpa(),
     lambda g: pins.test_split_then_merge_equals_unsplit(48),
     lambda g: pins.test_paged_prefill_equals_masked_sdpa((7, 40, 100), (7, 13, 1), 16),
+    lambda g: pins.test_window_decode_equals_masked_sdpa_and_split_merge(7),
 ]
 
 

@@ -530,6 +530,74 @@ def test_paged_prefill_brute_force_and_permutation():
 
 
 # ---------------------------------------------------------------------------
+# sliding window (keys max(0, p - W + 1) .. p)
+# ---------------------------------------------------------------------------
+def page_window_mask(rows, keys, window, offset=0):
+    """The page's construction, written out: for row i (at position offset + i)
+    the keys start = max(0, pos - window + 1) .. pos are open, the rest closed."""
+    allowed = torch.zeros((rows, keys), dtype=torch.bool)
+    for i in range(rows):
+        pos = offset + i
+        start = max(0, pos - window + 1)
+        allowed[i, start:pos + 1] = True
+    return allowed
+
+
+@pytest.mark.parametrize("window", [1, 5, 64, 1000])
+def test_window_prefill_and_paged_prefill_equal_masked_sdpa(window):
+    rng = np.random.default_rng(31)
+    Hq, Hkv, d, bs = 4, 2, 16, 8
+    ctxs, chunks = (9, 70, 130), (9, 20, 77)
+    Ks, Vs, kp, vp, tables, ctx, cu, q = _paged_prefill_inputs(rng, ctxs, chunks, Hq, Hkv, d, bs)
+    pout, plse = oracle.paged_prefill(q, kp, vp, tables, cu, ctx, bs, 0.3, oracle.F32, window=window)
+    # the full-sequence chunk (first sequence) also goes through the varlen prefill
+    fout, flse = oracle.prefill(q[:9], Ks[0], Vs[0], np.array([0, 9], np.int32), 0.3, oracle.F32, window=window)
+    np.testing.assert_allclose(fout, pout[:9], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(flse, plse[:9], rtol=0, atol=1e-12)
+    for s, (n, lq) in enumerate(zip(ctxs, chunks)):
+        a = int(cu[s])
+        Q = torch.from_numpy(q[a:a + lq].astype(np.float64)).permute(1, 0, 2)
+        K = torch.from_numpy(Ks[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(2, 0)
+        V = torch.from_numpy(Vs[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(2, 0)
+        allowed = page_window_mask(lq, n, window, offset=n - lq)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q[None], K[None], V[None], attn_mask=allowed,
+                                                                scale=0.3)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(pout[a:a + lq], ref, rtol=0, atol=1e-12)
+        S = ((Q @ K.transpose(1, 2)) * 0.3).masked_fill(~allowed, float("-inf"))
+        np.testing.assert_allclose(plse[a:a + lq], torch.logsumexp(S, -1).T.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 7, 40, 500])
+def test_window_decode_equals_masked_sdpa_and_split_merge(window):
+    rng = np.random.default_rng(32)
+    Hq, Hkv, d, bs, lens = 4, 2, 16, 16, (1, 17, 33, 130)
+    Ks = [rand_f32(rng, n, Hkv, d) for n in lens]
+    Vs = [rand_f32(rng, n, Hkv, d) for n in lens]
+    q = rand_f32(rng, len(lens), Hq, d)
+    kp, vp, tables, ctx = paged_batch(Ks, Vs, bs, rng)
+    out, lse = oracle.decode(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32, window=window)
+    for b, n in enumerate(lens):
+        allowed = page_window_mask(1, n, window, offset=n - 1)[0]
+        Kw, Vw = Ks[b][allowed.numpy()], Vs[b][allowed.numpy()]
+        ref_out, ref_lse = sdpa_decode_reference(q[b:b + 1], [Kw], [Vw], 0.25)
+        np.testing.assert_allclose(out[b], ref_out[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], ref_lse[0], rtol=0, atol=1e-12)
+    for ps in (16, 32):
+        po, pl = oracle.decode_partitions(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32, ps, window=window)
+        mo, ml = oracle.reduce_partitions(po, pl, ctx, ps)
+        np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-12)
+    # a window of one key returns the newest value; a window past the start changes nothing
+    o1, _ = oracle.decode(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32, window=1)
+    for b, n in enumerate(lens):
+        np.testing.assert_array_equal(o1[b], np.repeat(Vs[b][n - 1], 2, axis=0).astype(np.float64))
+    ow, lw = oracle.decode(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32, window=130)
+    on, ln = oracle.decode(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32)
+    np.testing.assert_array_equal(ow, on)
+    np.testing.assert_array_equal(lw, ln)
+
+
+# ---------------------------------------------------------------------------
 # the generator itself
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,over", [
