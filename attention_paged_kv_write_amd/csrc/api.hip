@@ -92,7 +92,20 @@ int paged_attention_decode(void* out, float* lse, float* part_out, float* part_l
                            int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                            int num_blocks, int partition_size, int max_context_len, float scale,
                            pa_dtype dtype, void* stream) {
+  return paged_attention_decode_window(out, lse, part_out, part_lse, q, k_cache, v_cache, block_tables,
+                                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, partition_size,
+                                       max_context_len, scale, 0, dtype, stream);
+}
+
+int paged_attention_decode_window(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                                  int num_blocks, int partition_size, int max_context_len, float scale,
+                                  int window, pa_dtype dtype, void* stream) {
   const char* fn = "paged_attention_decode";
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
@@ -144,6 +157,7 @@ int paged_attention_decode(void* out, float* lse, float* part_out, float* part_l
   a.max_context_len = max_context_len;
   a.scale_log2 = scale * pa::kLog2e;
   a.flat_units = 0;
+  a.window = window;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s)
@@ -184,7 +198,16 @@ int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k, c
                           const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
                           int num_q_heads, int num_kv_heads, int head_dim, float scale,
                           pa_dtype dtype, void* stream) {
+  return varlen_causal_prefill_window(out, lse, q, k, v, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                      num_q_heads, num_kv_heads, head_dim, scale, 0, dtype, stream);
+}
+
+int varlen_causal_prefill_window(void* out, float* lse, const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
+                                 int num_q_heads, int num_kv_heads, int head_dim, float scale, int window,
+                                 pa_dtype dtype, void* stream) {
   const char* fn = "varlen_causal_prefill";
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
@@ -220,6 +243,7 @@ int varlen_causal_prefill(void* out, float* lse, const void* q, const void* k, c
   a.max_blocks_per_seq = 0;
   a.num_blocks = 0;
   a.max_context_len = 0;
+  a.window = window;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_prefill_generic(a, dt, head_dim, s)
@@ -232,7 +256,20 @@ int paged_prefill(void* out, float* lse, const void* q, const void* k_cache, con
                   int num_seqs, int total_q, int max_seqlen_q, int num_q_heads, int num_kv_heads,
                   int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
                   int max_context_len, float scale, pa_dtype dtype, void* stream) {
+  return paged_prefill_window(out, lse, q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
+                              num_seqs, total_q, max_seqlen_q, num_q_heads, num_kv_heads, head_dim,
+                              block_size, max_blocks_per_seq, num_blocks, max_context_len, scale, 0,
+                              dtype, stream);
+}
+
+int paged_prefill_window(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* cu_seqlens_q,
+                         const int32_t* context_lens, int num_seqs, int total_q, int max_seqlen_q,
+                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int max_blocks_per_seq, int num_blocks, int max_context_len, float scale,
+                         int window, pa_dtype dtype, void* stream) {
   const char* fn = "paged_prefill";
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
@@ -274,6 +311,7 @@ int paged_prefill(void* out, float* lse, const void* q, const void* k_cache, con
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
+  a.window = window;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_paged_prefill_generic(a, dt, head_dim, s)

@@ -48,8 +48,12 @@ __device__ __forceinline__ void unpack16(const u32x4 w, float* f) {
   }
 }
 
+// Positions lo .. ctx-1 are visible (lo > 0 only under a sliding window:
+// the query at ctx-1 keeps its last `window` keys, "PageAttention +
+// FlashAttention golden combination", section 4.1); blocks wholly before lo
+// are never read.
 struct Range {
-  int ctx, blk_lo, blk_hi;
+  int ctx, lo, blk_lo, blk_hi;
 };
 
 __device__ __forceinline__ Range work_range(const DecodeArgs& a, int b, int part) {
@@ -58,15 +62,30 @@ __device__ __forceinline__ Range work_range(const DecodeArgs& a, int b, int part
   const int nblk = (ctx + a.block_size - 1) / a.block_size;
   Range r;
   r.ctx = ctx;
+  r.lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+  const int wblk = r.lo / a.block_size;
   if (a.partition_size > 0) {
     const int per = a.partition_size / a.block_size;
-    r.blk_lo = part * per;
-    r.blk_hi = min(nblk, r.blk_lo + per);
+    r.blk_lo = max(part * per, wblk);
+    r.blk_hi = min(nblk, part * per + per);
   } else {
-    r.blk_lo = 0;
+    r.blk_lo = wblk;
     r.blk_hi = nblk;
   }
   return r;
+}
+
+// A live partition (it starts before ctx) that the window leaves empty still
+// hands the merge a partial: out 0, lse -inf.
+template <int D, int G>
+__device__ __forceinline__ void store_empty_partial(const DecodeArgs& a, int b, int g, int part) {
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D;
+    const int e = idx - h * D;
+    const size_t pr = (static_cast<size_t>(b) * a.num_q_heads + g * G + h) * a.num_partitions + part;
+    a.part_out[pr * D + e] = 0.f;
+    if (e == 0) a.part_lse[pr] = kNegInf;
+  }
 }
 
 // Split-KV work unit u of a flat launch: the whole partitions of every
@@ -202,6 +221,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   const Range r = work_range(a, b, part);
   if (r.blk_lo >= r.blk_hi) {
     if (a.partition_size == 0) store_empty<BF, D, G>(a, b, g);
+    else if (part * a.partition_size < r.ctx) store_empty_partial<D, G>(a, b, g, part);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -240,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int row = r0 + c * TPW + rg;
-        valid[c] = row < BS && blk * BS + row < r.ctx;
+        valid[c] = row < BS && blk * BS + row < r.ctx && blk * BS + row >= r.lo;
         float kf[VEC];
         if (valid[c]) {
           unpack16<BF>(kc[slab + static_cast<size_t>(row) * ROW_CHUNKS + dl], kf);
@@ -429,8 +449,9 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       qf[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  int ids_lo = blk_lo;   // first block of the id window; moves up under a window
   auto load_ids = [&](int w0) -> int {
-    const int e = blk_lo + wave + W * (w0 + lane);
+    const int e = ids_lo + wave + W * (w0 + lane);
     return e < a.max_blocks_per_seq ? table[e] : -1;
   };
   int ids = load_ids(0);
@@ -439,7 +460,13 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   (void)ctx_raw;
   if (r.blk_lo >= r.blk_hi) {
     if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
+    else if (part * a.partition_size < r.ctx) store_empty_partial<D, G>(a, b, g, part);
     return;
+  }
+  // a sliding window starts the span past the speculated first block
+  if (r.blk_lo != ids_lo) {
+    ids_lo = r.blk_lo;
+    ids = load_ids(0);
   }
   const int span = r.blk_hi - r.blk_lo;
   const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;
@@ -522,7 +549,10 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       // st[i]: score of token pos0 + 4j + i for column c16
       float s[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (pos0 + 4 * j + i < lim) ? st[i] * a.scale_log2 : kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        const int pos = pos0 + 4 * j + i;
+        s[i] = (pos < lim && pos >= r.lo) ? st[i] * a.scale_log2 : kNegInf;
+      }
       const float mx = quarter_max(vmax3(vmax3(s[0], s[1], s[2]), s[3], s[3]));
       // lazy rescale: the running max moves (with l and O) only when some
       // column's tile max exceeds it by more than the slack

@@ -42,6 +42,7 @@ struct DecodeArgs {
   int max_context_len;
   float scale_log2;      // scale * log2(e)
   int flat_units;        // split-KV MFMA kernel: 1-D grid of balanced work units
+  int window;            // sliding window in keys (0 = none)
 };
 
 struct ReduceArgs {
@@ -77,6 +78,7 @@ struct PrefillArgs {
   int max_blocks_per_seq;
   int num_blocks;
   int max_context_len;
+  int window;                   // sliding window in keys (0 = none)
 };
 
 enum class DType { F32 = 0, BF16 = 1 };

@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int qw0 = qt * PM;   // the workgroup's first row
   const KeySpan ks = key_span<PAGED>(a, s, sp.len);
   if (ks.ctx == 0) return;
+  const int win = a.window;   // sliding window in keys, 0 = none
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
@@ -249,32 +250,34 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sv[nt][i] = sacc[nt][rg][i] * sl2;
-          if (masked && kt * kPN + 16 * nt + 4 * j + i > qrow) sv[nt][i] = kNegInf;
+          const int key = kt * kPN + 16 * nt + 4 * j + i;
+          if (masked && (key > qrow || (win > 0 && key <= qrow - win))) sv[nt][i] = kNegInf;
         }
       float mx = vmax3(vmax3(sv[0][0], sv[0][1], sv[0][2]), vmax3(sv[0][3], sv[1][0], sv[1][1]),
                        vmax3(sv[1][2], sv[1][3], sv[2][0]));
       mx = vmax3(mx, vmax3(sv[2][1], sv[2][2], sv[2][3]), vmax3(sv[3][0], sv[3][1], vmax3(sv[3][2], sv[3][3], sv[3][3])));
       mx = quarter_max(mx);
       // lazy rescale: the whole wave moves its maxima only when some row's
-      // max has grown past the slack.  The first tile holds key 0, visible to
-      // every row, so m leaves -inf there (alpha = 0); a row with no visible
-      // key in a later masked tile has mx = -inf and keeps its m.
+      // max has grown past the slack.  A row with no visible key in a masked
+      // tile has mx = -inf and keeps its m, which stays -inf until the row's
+      // first visible key (possible only under a sliding window).
       const uint64_t grow = __builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack);
       if (grow) {
         const float m_new = fmaxf(m[rg], mx);
-        const float alpha = fast_exp2(m[rg] - m_new);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m[rg] - m_new);
         m[rg] = m_new;
         l[rg] *= alpha;
 #pragma unroll
         for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
       }
+      const float ms = m[rg] == kNegInf ? 0.f : m[rg];
       uint32_t pw[4][2];
       float ps[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[nt][i] - m[rg]);   // masked: exp2(-inf) = 0
+        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[nt][i] - ms);   // masked: exp2(-inf) = 0
         ps[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
         pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
@@ -310,12 +313,20 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // row's position need the causal mask (one tile when pos0 = 0, since q0 is
   // a multiple of 32; at most two otherwise), later ones are skipped (every
   // wave still joins each barrier).
+  // A sliding window of `win` keys also hides keys <= position - win: tiles
+  // before the first row's window are skipped, tiles that reach into the last
+  // row's window start are masked.  The workgroup starts at its first wave's
+  // first needed tile.
   const bool wave_live = sp.len > q0;   // else every row of the wave is padding
-  const int n_full = wave_live ? (ks.pos0 + q0 + 1) >> 6 : 0;
-  const int kt_last = wave_live ? (ks.pos0 + min(q0 + 31, sp.len - 1)) >> 6 : -1;
-  load_ids(0, ids_cur);
-  issue(0, kvbuf);   // the first tile's loads overlap the Q loads
-  if (nkt > 1) load_ids(1, ids_next);
+  const int p_first = ks.pos0 + q0, p_last = ks.pos0 + min(q0 + 31, sp.len - 1);
+  const int kt_first = win > 0 ? max(0, p_first - win + 1) >> 6 : 0;
+  const int kt_wfull = win > 0 ? (max(0, p_last - win + 1) + kPN - 1) >> 6 : 0;
+  const int kt_cfull = (p_first + 1) >> 6;   // tiles below are causally full
+  const int kt_last = wave_live ? p_last >> 6 : -1;
+  const int kt0 = win > 0 ? max(0, ks.pos0 + qw0 - win + 1) >> 6 : 0;
+  load_ids(kt0, ids_cur);
+  issue(kt0, kvbuf + (kt0 & 1) * 2048);   // the first tile's loads overlap the Q loads
+  if (kt0 + 1 < nkt) load_ids(kt0 + 1, ids_next);
 
   // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.  Rows past
   // the sequence load its last row (all eight loads in flight at once) and are
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     }
   }
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = kt0; kt < nkt; ++kt) {
     wait_dma_all();
     __syncthreads();
     if (kt + 1 < nkt) {
@@ -346,8 +357,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       issue(kt + 1, kvbuf + ((kt + 1) & 1) * 2048);
       if (kt + 2 < nkt) load_ids(kt + 2, ids_next);
     }
-    if (kt < n_full) tile(kt, false);
-    else if (kt <= kt_last) tile(kt, true);
+    if (kt < kt_first || kt > kt_last) continue;   // nothing visible to this wave
+    if (kt >= kt_wfull && kt < kt_cfull) tile(kt, false);
+    else tile(kt, true);
   }
 
   uint16_t* out = static_cast<uint16_t*>(a.out);
@@ -388,7 +400,8 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int
   if (i >= sp.len) return;
   const KeySpan ks = key_span<PAGED>(a, s, sp.len);
   if (ks.ctx == 0) return;
-  const int last = ks.pos0 + i;   // the row sees keys 0 .. last
+  const int last = ks.pos0 + i;   // the row sees keys first .. last
+  const int first = a.window > 0 ? max(0, last - a.window + 1) : 0;
   const int32_t* table = PAGED ? a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq : nullptr;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int g = h / group;
@@ -403,7 +416,7 @@ __global__ __launch_bounds__(256) void prefill_generic_kernel(PrefillArgs a, int
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-  for (int k0 = 0; k0 <= last; k0 += TPW) {
+  for (int k0 = first; k0 <= last; k0 += TPW) {
     const int key = k0 + rg;
     const bool valid = key <= last;
     float kf[VEC], vf[VEC];

@@ -24,7 +24,8 @@ PA_OPT_FORCE_VECTOR_PATH = 1
 EXPORTED_SYMBOLS = (
     "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
-    "paged_prefill",
+    "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
+    "paged_prefill_window",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,6 +68,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_prefill.restype = i32
     lib.paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                   i32, i32, i32, i32, f32, i32, vp]
+    lib.paged_attention_decode_window.restype = i32
+    lib.paged_attention_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                  f32, i32, i32, vp]
+    lib.varlen_causal_prefill_window.restype = i32
+    lib.varlen_causal_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                 f32, i32, i32, vp]
+    lib.paged_prefill_window.restype = i32
+    lib.paged_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, i32, i32, i32, f32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -141,9 +152,10 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            partition_size: int = 0, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            part_out: Optional[torch.Tensor] = None,
-                           part_lse: Optional[torch.Tensor] = None
+                           part_lse: Optional[torch.Tensor] = None, window: int = 0
                            ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """PagedAttention decode.  Returns (out, lse), or (part_out, part_lse) when split."""
+    """PagedAttention decode.  Returns (out, lse), or (part_out, part_lse) when split.
+    window > 0 keeps only the last `window` positions (sliding window)."""
     lib = load_library()
     dt = _dtype_code(q)
     B, Hq, d = q.shape
@@ -179,9 +191,9 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             raise ValueError("paged_attention_decode: out/lse shape")
         po = _dev(out, "out", q.dtype)
         pl = _dev(lse, "lse", torch.float32)
-    _check(lib.paged_attention_decode(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
-                                      block_tables.shape[1], NB, int(partition_size),
-                                      int(max_context_len), float(scale), dt, _stream(q)))
+    _check(lib.paged_attention_decode_window(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
+                                             block_tables.shape[1], NB, int(partition_size),
+                                             int(max_context_len), float(scale), int(window), dt, _stream(q)))
     if partition_size > 0:
         return part_out, part_lse
     return out, lse
@@ -213,8 +225,10 @@ def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
 def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           cu_seqlens: torch.Tensor, max_seqlen: int,
                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                          lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Causal attention over sequences packed by cu_seqlens -> (out [T,H_q,d], lse [T,H_q])."""
+                          lse: Optional[torch.Tensor] = None,
+                          window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal attention over sequences packed by cu_seqlens -> (out [T,H_q,d], lse [T,H_q]).
+    window > 0 keeps only the last `window` keys of each row (sliding window)."""
     lib = load_library()
     dt = _dtype_code(q)
     T, Hq, d = q.shape
@@ -229,11 +243,11 @@ def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    _check(lib.varlen_causal_prefill(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
-                                     _dev(q, "q", ndim=3), _dev(k, "k", ndim=3), _dev(v, "v", ndim=3),
-                                     _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
-                                     cu_seqlens.shape[0] - 1, T, int(max_seqlen), Hq, Hkv, d,
-                                     float(scale), dt, _stream(q)))
+    _check(lib.varlen_causal_prefill_window(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
+                                            _dev(q, "q", ndim=3), _dev(k, "k", ndim=3), _dev(v, "v", ndim=3),
+                                            _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
+                                            cu_seqlens.shape[0] - 1, T, int(max_seqlen), Hq, Hkv, d,
+                                            float(scale), int(window), dt, _stream(q)))
     return out, lse
 
 
@@ -241,9 +255,9 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor, context_lens: torch.Tensor,
                   max_seqlen_q: int, max_context_len: int, scale: Optional[float] = None,
                   out: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  lse: Optional[torch.Tensor] = None, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """A chunk of query rows per sequence (the last rows of its cache) against its
-    paged cache -> (out [T_q,H_q,d], lse [T_q,H_q])."""
+    paged cache -> (out [T_q,H_q,d], lse [T_q,H_q]); window > 0: sliding window."""
     lib = load_library()
     dt = _dtype_code(q)
     T, Hq, d = q.shape
@@ -260,12 +274,12 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    _check(lib.paged_prefill(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
+    _check(lib.paged_prefill_window(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
                              _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
                              _dev(v_cache, "v_cache", ndim=4),
                              _dev(block_tables, "block_tables", torch.int32, 2),
                              _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1),
                              _dev(context_lens, "context_lens", torch.int32, 1),
                              S, T, int(max_seqlen_q), Hq, Hkv, d, bs, block_tables.shape[1], NB,
-                             int(max_context_len), float(scale), dt, _stream(q)))
+                             int(max_context_len), float(scale), int(window), dt, _stream(q)))
     return out, lse

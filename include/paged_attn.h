@@ -8,6 +8,7 @@
  *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
  * and a fifth extends prefill to a cached prefix:
  *   paged_prefill           a chunk of query rows against its sequence's paged cache
+ * The three attention calls also come in *_window forms (sliding window).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -222,6 +223,38 @@ int paged_prefill(void* out, float* lse, const void* q, const void* k_cache,
                   int total_q, int max_seqlen_q, int num_q_heads, int num_kv_heads,
                   int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
                   int max_context_len, float scale, pa_dtype dtype, void* stream);
+
+/*
+ * Sliding-window variants.  Identical to paged_attention_decode, varlen_causal_prefill
+ * and paged_prefill (which are these with window = 0), except that a query at position
+ * p attends only to positions max(0, p - window + 1) .. p: the last `window` keys, the
+ * mask that "PageAttention + FlashAttention golden combination" (section 4.1) builds.
+ * window = 0 means no window; window < 0 is PA_ERR_INVALID_ARG.  Blocks wholly outside
+ * the window are not read.  In split decode, a partition wholly before the window
+ * still writes its partial (part_out 0, part_lse -inf), so paged_attention_reduce
+ * merges the window's partials unchanged.
+ */
+int paged_attention_decode_window(void* out, float* lse, float* part_out, float* part_lse,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  int partition_size, int max_context_len, float scale,
+                                  int window, pa_dtype dtype, void* stream);
+
+int varlen_causal_prefill_window(void* out, float* lse, const void* q, const void* k,
+                                 const void* v, const int32_t* cu_seqlens, int num_seqs,
+                                 int total_tokens, int max_seqlen, int num_q_heads,
+                                 int num_kv_heads, int head_dim, float scale, int window,
+                                 pa_dtype dtype, void* stream);
+
+int paged_prefill_window(void* out, float* lse, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* cu_seqlens_q, const int32_t* context_lens, int num_seqs,
+                         int total_q, int max_seqlen_q, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                         int max_context_len, float scale, int window, pa_dtype dtype,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -135,6 +135,16 @@ def test_paged_prefill_validation(lib):
     assert call(T=0, mq=0) == 0
 
 
+def test_window_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.paged_attention_decode_window(p, p, p, p, p, p, p, p, p, 2, 8, 2, 128, 16, 4, 10, 0, 64, 0.1,
+                                             -1, 1, None) == 1
+    assert lib.varlen_causal_prefill_window(p, p, p, p, p, p, 2, 100, 60, 32, 8, 128, 0.1, -5, 1, None) == 1
+    assert lib.paged_prefill_window(p, p, p, p, p, p, p, p, 2, 100, 60, 32, 8, 128, 16, 8, 20, 128, 0.1, -1,
+                                    1, None) == 1
+    assert lib.varlen_causal_prefill_window(p, p, p, p, p, p, 0, 100, 60, 32, 8, 128, 0.1, 7, 1, None) == 0
+
+
 def test_option(lib):
     assert lib.pa_set_option(99, 1) == 1
     assert lib.pa_set_option(ops.PA_OPT_FORCE_VECTOR_PATH, 0) == 0
