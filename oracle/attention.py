@@ -33,7 +33,10 @@ Readings of points the pages leave open:
     so row i sees positions 0..ctx-Lq+i (the causal mask aligned to the end);
   * a sliding window of W keys (0 = none) keeps positions max(0, p-W+1)..p
     for a query at position p; a split partition wholly before the window is
-    empty (out 0, lse -inf).
+    empty (out 0, lse -inf), and the window-aware merge starts at the first
+    partition the window reaches;
+  * keys before the window take no part in any sum, so their blocks are
+    never fetched: their table entries may name freed blocks (any value).
 
 Every function here has a pin in tests/test_oracle_pins.py (nothing is left
 parity-unpinned).
@@ -86,17 +89,18 @@ def kv_write(k_cache, v_cache, k, v, slot_mapping, block_size):
 # ---------------------------------------------------------------------------
 # a0 / a2: logical -> physical gather through the block table
 # ---------------------------------------------------------------------------
-def gather(pool, table_row, ctx, block_size):
-    """Rows 0..ctx-1 of one sequence, fetched through its block table.
+def gather(pool, table_row, ctx, block_size, start=0):
+    """Rows start..ctx-1 of one sequence, fetched through its block table.
 
     Logical page p // block_size maps to the physical block the table names
     ("Llama 4 inference doubling ...", section 3.1: logical page number to
     physical block number, int32, -1 = unallocated).  Returns
-    ``[ctx, H_kv, d]`` in the pool's storage dtype.
+    ``[ctx - start, H_kv, d]`` in the pool's storage dtype; pages before
+    ``start`` are not looked up.
     """
     num_blocks = pool.shape[0]
     rows = []
-    for p in range(int(ctx)):
+    for p in range(int(start), int(ctx)):
         blk = int(table_row[p // block_size])
         if not 0 <= blk < num_blocks:
             raise IndexError(f"position {p}: block id {blk} outside [0, {num_blocks})")
@@ -184,8 +188,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
     for b in range(B):
         ctx = int(context_lens[b])
         lo = window_start(ctx - 1, window) if ctx > 0 else 0
-        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)[lo:]
-        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)[lo:]
+        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size, lo), dtype)
+        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size, lo), dtype)
         for h in range(Hq):
             g = group_of(h, Hq, Hkv)
             o, l, p = attend(upcast(q[b, h], dtype), Kall[:, g, :], Vall[:, g, :], scale)
@@ -219,45 +223,50 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
     part_lse = np.full((B, Hq, P), -math.inf)
     for b in range(B):
         ctx = int(context_lens[b])
-        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size), dtype)
-        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size), dtype)
         wlo = window_start(ctx - 1, window) if ctx > 0 else 0
+        # Kall[i] holds position wlo + i
+        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size, wlo), dtype)
+        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size, wlo), dtype)
         for i in range(P):
             lo, hi = max(i * partition_size, wlo), min((i + 1) * partition_size, ctx)
             if lo >= hi:
                 continue
             for h in range(Hq):
                 g = group_of(h, Hq, Hkv)
-                o, l, _ = attend(upcast(q[b, h], dtype), Kall[lo:hi, g, :],
-                                 Vall[lo:hi, g, :], scale)
+                o, l, _ = attend(upcast(q[b, h], dtype), Kall[lo - wlo:hi - wlo, g, :],
+                                 Vall[lo - wlo:hi - wlo, g, :], scale)
                 part_out[b, h, i], part_lse[b, h, i] = o, l
     return part_out, part_lse
 
 
-def reduce_partitions(part_out, part_lse, context_lens, partition_size):
+def reduce_partitions(part_out, part_lse, context_lens, partition_size, window=0):
     """Merge partition results by log-sum-exp.
 
     With M the largest partition lse and w_i = exp(lse_i - M) (0 for a
     partition past the end of the sequence), the merged output is
     sum_i w_i o_i / sum_i w_i and the merged lse is M + log(sum_i w_i).  The
     LSE that the varlen interface returns ("Llama 4 inference doubling ...",
-    section 2.4) is what makes this merge exact.
+    section 2.4) is what makes this merge exact.  With a sliding window the
+    merge starts at the partition holding the window's first key: the ones
+    before it are empty by definition and are not read.
     """
     B, Hq, P, d = part_out.shape
     out = np.zeros((B, Hq, d))
     lse = np.full((B, Hq), -math.inf)
     for b in range(B):
-        live = min(P, -(-int(context_lens[b]) // int(partition_size)))
-        if live <= 0:
+        ctx = int(context_lens[b])
+        live = min(P, -(-ctx // int(partition_size)))
+        first = window_start(ctx - 1, window) // int(partition_size) if ctx > 0 else 0
+        if live <= first:
             continue
         for h in range(Hq):
-            l = np.asarray(part_lse[b, h, :live], dtype=np.float64)
+            l = np.asarray(part_lse[b, h, first:live], dtype=np.float64)
             M = l.max()
             if M == -math.inf:
                 continue
             w = np.exp(l - M)
             W = w.sum()
-            out[b, h] = (w[:, None] * np.asarray(part_out[b, h, :live], dtype=np.float64)).sum(0) / W
+            out[b, h] = (w[:, None] * np.asarray(part_out[b, h, first:live], dtype=np.float64)).sum(0) / W
             lse[b, h] = M + math.log(W)
     return out, lse
 
@@ -335,16 +344,19 @@ def paged_prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, context_lens,
             continue
         if Lq > ctx:
             raise ValueError(f"sequence {s}: {Lq} query rows but only {ctx} cached positions")
+        # the first row's window start: no row sees a key before it
+        k0 = window_start(ctx - Lq, window)
+        keys = np.arange(k0, ctx)[None, :]                               # key positions
         for h in (range(Hq) if heads is None else heads):
             g = group_of(h, Hq, Hkv)
-            K = upcast(gather(k_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0, :]
-            V = upcast(gather(v_cache[:, g:g + 1], block_tables[s], ctx, block_size), dtype)[:, 0, :]
+            K = upcast(gather(k_cache[:, g:g + 1], block_tables[s], ctx, block_size, k0), dtype)[:, 0, :]
+            V = upcast(gather(v_cache[:, g:g + 1], block_tables[s], ctx, block_size, k0), dtype)[:, 0, :]
             Q = upcast(q[a:e, h, :], dtype)
-            scores = scale * (Q @ K.T)                                   # [Lq, ctx]
+            scores = scale * (Q @ K.T)                                   # [Lq, ctx - k0]
             pos = ctx - Lq + np.arange(Lq)[:, None]                      # row positions
-            scores[np.arange(ctx)[None, :] > pos] = -np.inf
+            scores[keys > pos] = -np.inf
             if window > 0:
-                scores[np.arange(ctx)[None, :] <= pos - window] = -np.inf
+                scores[keys <= pos - window] = -np.inf
             m = scores.max(axis=1, keepdims=True)
             w = np.exp(scores - m)
             z = w.sum(axis=1, keepdims=True)

@@ -35,9 +35,9 @@ def _group_mod(h, num_q_heads, num_kv_heads):
     return h % (num_q_heads // num_kv_heads)
 
 
-def _gather_swapped(pool, table_row, ctx, block_size):
+def _gather_swapped(pool, table_row, ctx, block_size, start=0):
     rows = []
-    for p in range(int(ctx)):
+    for p in range(int(start), int(ctx)):
         blk = int(table_row[p % block_size]) if p % block_size < len(table_row) else 0
         rows.append(pool[blk, :, p // block_size % block_size, :])
     if not rows:
@@ -108,9 +108,23 @@ def _window_start_off_by_one(pos, window):
     return max(0, int(pos) - int(window)) if window > 0 else 0
 
 
-def _reduce_counts_dead(part_out, part_lse, context_lens, partition_size):
+def _reduce_counts_dead(part_out, part_lse, context_lens, partition_size, window=0):
     B, Hq, P, d = part_out.shape
-    return oa.__dict__["_orig_reduce"](part_out, part_lse, np.full(B, P * partition_size), partition_size)
+    return oa.__dict__["_orig_reduce"](part_out, part_lse, np.full(B, P * partition_size), partition_size,
+                                       window)
+
+
+def _reduce_window_skips_first_partition(part_out, part_lse, context_lens, partition_size, window=0):
+    # the merge starts one partition late under a window
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if window > 0:
+        lens = np.where(lens > 0, lens, 0)
+        shifted = np.maximum(lens - 1 - window + 1, 0) // partition_size
+        po, pl = part_out.copy(), part_lse.copy()
+        for b, f in enumerate(shifted):
+            pl[b, :, :f + 1] = -np.inf
+        return oa.__dict__["_orig_reduce"](po, pl, context_lens, partition_size, 0)
+    return oa.__dict__["_orig_reduce"](part_out, part_lse, context_lens, partition_size, window)
 
 
 MUTANTS = {
@@ -125,6 +139,7 @@ MUTANTS = {
     "merge_counts_dead_partitions": [("reduce_partitions", _reduce_counts_dead)],
     "paged_prefill_mask_top_left": [("paged_prefill", _paged_prefill_top_left)],
     "window_one_key_too_many": [("window_start", _window_start_off_by_one)],
+    "window_merge_skips_first_partition": [("reduce_partitions", _reduce_window_skips_first_partition)],
 }
 
 PIN_CALLS = [
@@ -140,6 +155,7 @@ PIN_CALLS = [
     lambda g: pins.test_split_then_merge_equals_unsplit(48),
     lambda g: pins.test_paged_prefill_equals_masked_sdpa((7, 40, 100), (7, 13, 1), 16),
     lambda g: pins.test_window_decode_equals_masked_sdpa_and_split_merge(7),
+    lambda g: pins.test_window_decode_equals_masked_sdpa_and_split_merge(40),
 ]
 
 

@@ -543,6 +543,15 @@ def page_window_mask(rows, keys, window, offset=0):
     return allowed
 
 
+def free_before_window(tables, first_keys, block_size):
+    """Tables whose entries for blocks ending at or before each sequence's
+    first visible key are -1 (blocks a server may have freed)."""
+    ft = tables.copy()
+    for b, k0 in enumerate(first_keys):
+        ft[b, :int(k0) // block_size] = -1
+    return ft
+
+
 @pytest.mark.parametrize("window", [1, 5, 64, 1000])
 def test_window_prefill_and_paged_prefill_equal_masked_sdpa(window):
     rng = np.random.default_rng(31)
@@ -565,6 +574,11 @@ def test_window_prefill_and_paged_prefill_equal_masked_sdpa(window):
         np.testing.assert_allclose(pout[a:a + lq], ref, rtol=0, atol=1e-12)
         S = ((Q @ K.transpose(1, 2)) * 0.3).masked_fill(~allowed, float("-inf"))
         np.testing.assert_allclose(plse[a:a + lq], torch.logsumexp(S, -1).T.numpy(), rtol=0, atol=1e-12)
+    # blocks before the first row's window may be freed
+    ft = free_before_window(tables, [max(0, n - lq - window + 1) for n, lq in zip(ctxs, chunks)], bs)
+    fo, fl = oracle.paged_prefill(q, kp, vp, ft, cu, ctx, bs, 0.3, oracle.F32, window=window)
+    np.testing.assert_array_equal(fo, pout)
+    np.testing.assert_array_equal(fl, plse)
 
 
 @pytest.mark.parametrize("window", [1, 7, 40, 500])
@@ -587,6 +601,19 @@ def test_window_decode_equals_masked_sdpa_and_split_merge(window):
         mo, ml = oracle.reduce_partitions(po, pl, ctx, ps)
         np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
         np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-12)
+        # the window-aware merge never reads the partitions before the window
+        first = [max(0, n - window) // ps for n in lens]
+        for b, f in enumerate(first):
+            po[b, :, :f], pl[b, :, :f] = np.nan, np.nan
+        mo, ml = oracle.reduce_partitions(po, pl, ctx, ps, window=window)
+        np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-12)
+    # blocks wholly before the window may be freed: their table entries are
+    # never looked up
+    ft = free_before_window(tables, [max(0, n - window) for n in lens], bs)
+    fo, fl = oracle.decode(q, kp, vp, ft, ctx, bs, 0.25, oracle.F32, window=window)
+    np.testing.assert_array_equal(fo, out)
+    np.testing.assert_array_equal(fl, lse)
     # a window of one key returns the newest value; a window past the start changes nothing
     o1, _ = oracle.decode(q, kp, vp, tables, ctx, bs, 0.25, oracle.F32, window=1)
     for b, n in enumerate(lens):
