@@ -168,7 +168,16 @@ int paged_attention_decode_window(void* out, float* lse, float* part_out, float*
 int paged_attention_reduce(void* out, float* lse, const float* part_out, const float* part_lse,
                            const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
                            int partition_size, int max_partitions, pa_dtype dtype, void* stream) {
+  return paged_attention_reduce_window(out, lse, part_out, part_lse, context_lens, num_seqs, num_q_heads,
+                                       head_dim, partition_size, max_partitions, 0, dtype, stream);
+}
+
+int paged_attention_reduce_window(void* out, float* lse, const float* part_out, const float* part_lse,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
+                                  int partition_size, int max_partitions, int window, pa_dtype dtype,
+                                  void* stream) {
   const char* fn = "paged_attention_reduce";
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || head_dim <= 0 || partition_size <= 0 || max_partitions <= 0)
@@ -190,6 +199,7 @@ int paged_attention_reduce(void* out, float* lse, const float* part_out, const f
   a.head_dim = head_dim;
   a.partition_size = partition_size;
   a.max_partitions = max_partitions;
+  a.window = window;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   return launch_status(pa::launch_reduce(a, dt, static_cast<hipStream_t>(stream)), fn);
 }

@@ -75,28 +75,39 @@ __device__ __forceinline__ Range work_range(const DecodeArgs& a, int b, int part
   return r;
 }
 
-// A live partition (it starts before ctx) that the window leaves empty still
-// hands the merge a partial: out 0, lse -inf.
-template <int D, int G>
-__device__ __forceinline__ void store_empty_partial(const DecodeArgs& a, int b, int g, int part) {
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int e = idx - h * D;
-    const size_t pr = (static_cast<size_t>(b) * a.num_q_heads + g * G + h) * a.num_partitions + part;
-    a.part_out[pr * D + e] = 0.f;
-    if (e == 0) a.part_lse[pr] = kNegInf;
-  }
-}
+// Partitions of a split launch that a sliding window leaves empty (wholly
+// before the window's first key) are not written; the window-aware merge
+// starts past them.
 
 // Split-KV work unit u of a flat launch: the whole partitions of every
-// sequence (sequence by sequence), then the partial last partitions.  Full
-// units first keeps the long work at the head of the dispatch order, and a
-// grid with no empty units in front lets every CU take an even share of the
-// bytes.  One wave computes it (lane l scans sequences l*K .. l*K+K-1);
-// returns b = -1 past the last unit.  At most 64*16 sequences.
+// sequence (sequence by sequence), then the partial ones.  Full units first
+// keeps the long work at the head of the dispatch order, and a grid with no
+// empty units in front lets every CU take an even share of the bytes.  Only
+// partitions that hold a visible key are units: under a sliding window the
+// live ones are lo/P .. ceil(ctx/P)-1, the full ones ceil(lo/P) .. ctx/P-1,
+// and the partial ones (at most two) the first live one when lo is not
+// aligned and the one holding ctx-1 when ctx is not.  One wave computes it
+// (lane l scans sequences l*K .. l*K+K-1); returns b = -1 past the last unit.
+// At most 64*16 sequences.
 struct Unit {
   int b, part;
 };
+
+// Live and full partition ranges of one sequence.
+struct PartSpan {
+  int f0, f1;   // live:  f0 .. f1-1
+  int c0, c1;   // full:  c0 .. c1-1 (empty when c1 <= c0)
+};
+
+__device__ __forceinline__ PartSpan part_span(int ctx, int window, int per) {
+  const int lo = window > 0 ? max(0, ctx - window) : 0;
+  PartSpan p;
+  p.f0 = lo / per;
+  p.f1 = (ctx + per - 1) / per;
+  p.c0 = (lo + per - 1) / per;
+  p.c1 = ctx / per;
+  return p;
+}
 
 __device__ __forceinline__ Unit flat_unit(const DecodeArgs& a, int u) {
   const int lane = threadIdx.x & 63;
@@ -108,9 +119,10 @@ __device__ __forceinline__ Unit flat_unit(const DecodeArgs& a, int u) {
   for (int k = 0; k < K; ++k) {
     const int sq = lane * K + k;
     if (sq < B) {
-      const int ctx = clampi(a.context_lens[sq], 0, cap);
-      nf += ctx / per;
-      np += (ctx % per) != 0;
+      const PartSpan ps = part_span(clampi(a.context_lens[sq], 0, cap), a.window, per);
+      const int full = max(0, ps.c1 - ps.c0);
+      nf += full;
+      np += max(0, ps.f1 - ps.f0) - full;
     }
   }
   // inclusive scans of the per-lane counts
@@ -134,9 +146,15 @@ __device__ __forceinline__ Unit flat_unit(const DecodeArgs& a, int u) {
   int rem = v - excl;
   for (int k = 0; k < K; ++k) {
     const int sq = owner * K + k;
-    const int ctx = sq < B ? clampi(a.context_lens[sq], 0, cap) : 0;
-    const int n = full ? ctx / per : ((ctx % per) != 0);
-    if (rem < n) return Unit{sq, full ? rem : ctx / per};
+    const PartSpan ps = part_span(sq < B ? clampi(a.context_lens[sq], 0, cap) : 0, a.window, per);
+    const int nfull = max(0, ps.c1 - ps.c0);
+    const int n = full ? nfull : max(0, ps.f1 - ps.f0) - nfull;
+    if (rem < n) {
+      // partial units: the unaligned first live partition (if any), then the
+      // one after the full range (or the second live one when none is full)
+      const int first_partial = ps.f0 < ps.c0 ? 1 : 0;
+      return Unit{sq, full ? ps.c0 + rem : (rem < first_partial ? ps.f0 : max(ps.c1, ps.c0))};
+    }
     rem -= n;
   }
   return Unit{-1, 0};
@@ -221,7 +239,6 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   const Range r = work_range(a, b, part);
   if (r.blk_lo >= r.blk_hi) {
     if (a.partition_size == 0) store_empty<BF, D, G>(a, b, g);
-    else if (part * a.partition_size < r.ctx) store_empty_partial<D, G>(a, b, g, part);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -460,7 +477,6 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   (void)ctx_raw;
   if (r.blk_lo >= r.blk_hi) {
     if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
-    else if (part * a.partition_size < r.ctx) store_empty_partial<D, G>(a, b, g, part);
     return;
   }
   // a sliding window starts the span past the speculated first block
@@ -650,10 +666,15 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     // flat grid of balanced units (one per KV head and live partition, in the
     // order flat_unit defines; the kernel maps ids past the last unit to no
     // work), unit-major so the KV heads of a unit spread over the XCDs
+    // A window of W keys leaves a sequence at most (W-1)/P + 2 live
+    // partitions (the window's keys start anywhere inside the first one).
     DecodeArgs f = a;
-    const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
+    int64_t per_seq = grid.z;
+    if (a.window > 0 && (a.window - 1) / a.partition_size + 2 < per_seq)
+      per_seq = (a.window - 1) / a.partition_size + 2;
+    const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
-    const dim3 fg = f.flat_units ? dim3(grid.x * grid.y * grid.z) : grid;
+    const dim3 fg = f.flat_units ? dim3(static_cast<unsigned>(nwg)) : grid;
     hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1>), fg, dim3(64), 0, s, f);
   } else
     hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4>), grid, dim3(256), 0, s, a);

@@ -56,6 +56,7 @@ struct ReduceArgs {
   int head_dim;
   int partition_size;
   int max_partitions;
+  int window;            // sliding window of keys (0 = none): merge from its first partition
 };
 
 struct PrefillArgs {

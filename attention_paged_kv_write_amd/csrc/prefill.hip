@@ -157,6 +157,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   bf16x8 qf[RG][4];   // Q^T B operands, loaded below (after the first tile is requested)
   const int kend = min(ks.pos0 + qw0 + PM, ks.ctx);   // keys 0 .. kend-1 are needed by the workgroup
   const int nkt = (kend + kPN - 1) / kPN;
+  // Under a window no row of the workgroup sees a key before kmin (its first
+  // row's window start): tile slots below it load key kmin instead (masked),
+  // so blocks wholly before the window are never touched and may be freed.
+  const int kmin = win > 0 ? max(0, ks.pos0 + qw0 - win + 1) : 0;
 
   // LDS-DMA of key tile kt: 2048 chunks (K then V); wave w issues slices
   // w, w+4, ..., each 64 lanes x 16 B.  Slice i holds rows 4(i%16) + lane/16 at
@@ -175,14 +179,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   auto load_ids = [&](int kt, int (&ids)[4]) {
     if constexpr (PAGED) {
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) ids[mm] = table[min(kt * kPN + drow + 16 * mm, ks.ctx - 1) >> lbs];
+      for (int mm = 0; mm < 4; ++mm) ids[mm] = table[min(max(kt * kPN + drow + 16 * mm, kmin), ks.ctx - 1) >> lbs];
     }
   };
   auto issue = [&](int kt, u32x4* buf) {
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
       const int row = drow + 16 * (ii & 3);
-      const int key = min(kt * kPN + row, ks.ctx - 1);
+      const int key = min(max(kt * kPN + row, kmin), ks.ctx - 1);
       size_t rowoff;
       if constexpr (PAGED) {
         int phys = ids_cur[ii & 3];
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int kt_wfull = win > 0 ? (max(0, p_last - win + 1) + kPN - 1) >> 6 : 0;
   const int kt_cfull = (p_first + 1) >> 6;   // tiles below are causally full
   const int kt_last = wave_live ? p_last >> 6 : -1;
-  const int kt0 = win > 0 ? max(0, ks.pos0 + qw0 - win + 1) >> 6 : 0;
+  const int kt0 = kmin >> 6;
   load_ids(kt0, ids_cur);
   issue(kt0, kvbuf + (kt0 & 1) * 2048);   // the first tile's loads overlap the Q loads
   if (kt0 + 1 < nkt) load_ids(kt0 + 1, ids_next);

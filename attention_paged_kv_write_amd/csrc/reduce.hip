@@ -6,6 +6,10 @@
 // ("Llama 4 inference doubling (FlashAttention-3 + PagedAttention + vLLM)",
 // section 2.4) is what makes the merge exact.
 //
+// Under a sliding window of W keys the merge covers partitions lo/P ..
+// ceil(ctx/P)-1 only (lo = max(0, ctx - W)): the ones before hold no visible
+// key and the decode call leaves them unwritten.
+//
 // General kernel: one workgroup per (sequence, query head).  Pass 1 finds M;
 // pass 2 turns a chunk of partition lse values into weights held in LDS; pass
 // 3 streams the partition outputs (each wave takes every fourth partition,
@@ -28,9 +32,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t ctx = max(a.context_lens[b], 0);
   const int64_t live = (ctx + a.partition_size - 1) / a.partition_size;
-  const int n = static_cast<int>(min<int64_t>(live, a.max_partitions));
-  const float* lse_row = a.part_lse + row * a.max_partitions;
-  const float* out_row = a.part_out + row * a.max_partitions * D;
+  const int64_t first = a.window > 0 ? max<int64_t>(0, ctx - a.window) / a.partition_size : 0;
+  const int n = static_cast<int>(max<int64_t>(0, min<int64_t>(live, a.max_partitions) - first));
+  const float* lse_row = a.part_lse + row * a.max_partitions + first;
+  const float* out_row = a.part_out + (row * a.max_partitions + first) * D;
 
   float mx = kNegInf;
   for (int i = tid; i < n; i += 256) mx = fmaxf(mx, lse_row[i]);
@@ -100,10 +105,11 @@ __global__ __launch_bounds__(256) void reduce_small_kernel(ReduceArgs a) {
   if (row >= static_cast<size_t>(a.num_seqs) * a.num_q_heads) return;
   const int b = static_cast<int>(row / a.num_q_heads);
   const int64_t ctx = max(a.context_lens[b], 0);
-  const int n = static_cast<int>(min<int64_t>((ctx + a.partition_size - 1) / a.partition_size,
-                                              min(a.max_partitions, MAXP)));
-  const float* lse_row = a.part_lse + row * a.max_partitions;
-  const float* out_row = a.part_out + row * a.max_partitions * D + lane * DPL;
+  const int64_t first = a.window > 0 ? max<int64_t>(0, ctx - a.window) / a.partition_size : 0;
+  const int64_t live = min<int64_t>((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+  const int n = static_cast<int>(min<int64_t>(max<int64_t>(0, live - first), MAXP));
+  const float* lse_row = a.part_lse + row * a.max_partitions + first;
+  const float* out_row = a.part_out + (row * a.max_partitions + first) * D + lane * DPL;
   const float my_lse = lane < n ? lse_row[lane] : kNegInf;
   float o[MAXP][DPL];
 #pragma unroll
@@ -151,13 +157,23 @@ __global__ __launch_bounds__(256) void reduce_small_kernel(ReduceArgs a) {
 
 namespace {
 
+// Most partitions one (sequence, head) can merge: all of them, or under a
+// window of W keys at most (W-1)/P + 2 (its first key can sit anywhere in the
+// first one).
+int64_t live_bound(const ReduceArgs& a) {
+  int64_t n = a.max_partitions;
+  if (a.window > 0 && (a.window - 1) / a.partition_size + 2 < n) n = (a.window - 1) / a.partition_size + 2;
+  return n;
+}
+
 template <bool BF, int D>
 hipError_t launch_small(const ReduceArgs& a, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
   const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
-  if (a.max_partitions <= 8)
+  const int64_t nb = live_bound(a);
+  if (nb <= 8)
     hipLaunchKernelGGL((reduce_small_kernel<BF, D, 8>), grid, dim3(256), 0, s, a);
-  else if (a.max_partitions <= 16)
+  else if (nb <= 16)
     hipLaunchKernelGGL((reduce_small_kernel<BF, D, 16>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((reduce_small_kernel<BF, D, 32>), grid, dim3(256), 0, s, a);
@@ -169,7 +185,7 @@ hipError_t launch_small(const ReduceArgs& a, hipStream_t s) {
 hipError_t launch_reduce(const ReduceArgs& a, DType dt, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.num_seqs) * a.num_q_heads));
   if (a.num_seqs == 0) return hipSuccess;
-  if (a.max_partitions <= 32 && (a.head_dim == 64 || a.head_dim == 128)) {
+  if (live_bound(a) <= 32 && (a.head_dim == 64 || a.head_dim == 128)) {
     if (dt == DType::BF16)
       return a.head_dim == 128 ? launch_small<true, 128>(a, s) : launch_small<true, 64>(a, s);
     return a.head_dim == 128 ? launch_small<false, 128>(a, s) : launch_small<false, 64>(a, s);

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
-    "paged_prefill_window",
+    "paged_prefill_window", "paged_attention_reduce_window",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.varlen_causal_prefill_window.restype = i32
     lib.varlen_causal_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  f32, i32, i32, vp]
+    lib.paged_attention_reduce_window.restype = i32
+    lib.paged_attention_reduce_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.paged_prefill_window.restype = i32
     lib.paged_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, i32, vp]
@@ -203,8 +205,11 @@ def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
                            context_lens: torch.Tensor, partition_size: int,
                            out_dtype: torch.dtype = torch.bfloat16,
                            out: Optional[torch.Tensor] = None,
-                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Log-sum-exp merge of split-KV partitions -> (out [B, H_q, d], lse [B, H_q])."""
+                           lse: Optional[torch.Tensor] = None,
+                           window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Log-sum-exp merge of split-KV partitions -> (out [B, H_q, d], lse [B, H_q]).
+    window: the sliding window the partitions were computed with (the merge
+    starts at the partition holding the window's first key)."""
     lib = load_library()
     B, Hq, P, d = part_out.shape
     if part_lse.shape != (B, Hq, P) or context_lens.shape != (B,):
@@ -214,11 +219,12 @@ def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=part_out.device)
     dt = _dtype_code(out)
-    _check(lib.paged_attention_reduce(_dev(out, "out", ndim=3), _dev(lse, "lse", torch.float32, 2),
-                                      _dev(part_out, "part_out", torch.float32, 4),
-                                      _dev(part_lse, "part_lse", torch.float32, 3),
-                                      _dev(context_lens, "context_lens", torch.int32, 1),
-                                      B, Hq, d, int(partition_size), P, dt, _stream(part_out)))
+    _check(lib.paged_attention_reduce_window(_dev(out, "out", ndim=3), _dev(lse, "lse", torch.float32, 2),
+                                             _dev(part_out, "part_out", torch.float32, 4),
+                                             _dev(part_lse, "part_lse", torch.float32, 3),
+                                             _dev(context_lens, "context_lens", torch.int32, 1),
+                                             B, Hq, d, int(partition_size), P, int(window), dt,
+                                             _stream(part_out)))
     return out, lse
 
 

@@ -103,6 +103,8 @@ class DecodeSpec:
     v_dist: str = "normal"
     partition_size: int = 0               # 0 = single pass; else split-KV
     pool_copies: int = 1                  # bench: independent copies (defeat MALL)
+    window: int = 0                       # sliding window of keys (0 = none)
+    free_before_window: bool = False      # blocks wholly before the window are unallocated (-1)
 
 
 @dataclass
@@ -140,6 +142,13 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
     nblk = (ctx.astype(np.int64) + bs - 1) // bs
     mbps = spec.max_blocks_per_seq or int(max(1, nblk.max()))
     assert nblk.max() <= mbps
+    # first allocated block: under a sliding window a server may free the
+    # blocks that end before the window's first key, ctx - window
+    if spec.window > 0 and spec.free_before_window:
+        assert not spec.share_group
+        first_blk = np.maximum(ctx.astype(np.int64) - spec.window, 0) // bs
+    else:
+        first_blk = np.zeros(B, dtype=np.int64)
 
     # 2. block ids: shared prefixes first, then private blocks, all permuted
     if spec.share_group:
@@ -148,7 +157,7 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
         assert (nblk >= spec.share_blocks).all()
         needed = n_groups * spec.share_blocks + int((nblk - spec.share_blocks).sum())
     else:
-        needed = int(nblk.sum())
+        needed = int((nblk - first_blk).sum())
     NB = spec.num_blocks or int(math.ceil(spec.pool_factor * needed))
     assert NB >= needed
     perm = rng.permutation(NB).astype(np.int32)
@@ -166,9 +175,9 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
             cursor += n_priv
     else:
         for b in range(B):
-            n = int(nblk[b])
-            tables[b, :n] = perm[cursor:cursor + n]
-            cursor += n
+            f, n = int(first_blk[b]), int(nblk[b])
+            tables[b, f:n] = perm[cursor:cursor + n - f]
+            cursor += n - f
 
     # 3. history K/V: iid draws over the whole pool, then NaN where unused
     shape = (NB, Hkv, bs, d)
@@ -179,7 +188,7 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
         n = int(ctx[b])
         # positions that hold history (the new token, if any, arrives by write)
         hist = n - 1 if (spec.write_new_token and n > 0) else n
-        for p0 in range(0, hist, bs):
+        for p0 in range(int(first_blk[b]) * bs, hist, bs):
             blk = tables[b, p0 // bs]
             used[blk, :min(bs, hist - p0)] = True
     nanv = nan_value(spec.dtype)
@@ -427,6 +436,14 @@ LONG_CONTEXT_SPLIT_DECODE = DecodeSpec(
     ctx_fixed=(131072,) * 4, num_blocks=40960, max_blocks_per_seq=8192,
     write_new_token=False, v_dist="uniform", partition_size=512)
 
+# Sliding-window decode with the window the golden-combination page uses
+# (2048 keys): Llama-3-8B heads, 64 sequences of 1024..16384 positions, split
+# into 256-key partitions; blocks wholly before each window are freed.
+LLAMA3_8B_WINDOW_DECODE = DecodeSpec(
+    name="llama3_8b_sliding_window_decode_bf16", dtype=BF16, batch=64, num_q_heads=32,
+    num_kv_heads=8, head_dim=128, block_size=16, ctx_min=1024, ctx_max=16384,
+    max_blocks_per_seq=1024, partition_size=256, window=2048, free_before_window=True)
+
 # Chunked prefill against a cached prefix (the first widening past the five):
 # Llama-3-8B heads, 16 sequences, 0..3072 cached positions, 128..1024 new rows.
 LLAMA3_8B_CHUNKED_PREFILL = PagedPrefillSpec(
@@ -441,6 +458,7 @@ CONFIGS = {
     4: LLAMA2_70B_PREFIX_DECODE,
     5: LONG_CONTEXT_SPLIT_DECODE,
     6: LLAMA3_8B_CHUNKED_PREFILL,
+    7: LLAMA3_8B_WINDOW_DECODE,
 }
 
 
@@ -449,7 +467,7 @@ def seed_for(config_index: int) -> int:
 
 
 def make_case(config_index: int, seed: Optional[int] = None, **overrides):
-    """Build workload ``config_index`` (1..6), optionally shrunk by overrides."""
+    """Build workload ``config_index`` (1..7), optionally shrunk by overrides."""
     spec = CONFIGS[config_index]
     if overrides:
         spec = replace(spec, **overrides)

@@ -8,7 +8,7 @@
  *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
  * and a fifth extends prefill to a cached prefix:
  *   paged_prefill           a chunk of query rows against its sequence's paged cache
- * The three attention calls also come in *_window forms (sliding window).
+ * The four attention calls also come in *_window forms (sliding window).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -229,10 +229,15 @@ int paged_prefill(void* out, float* lse, const void* q, const void* k_cache,
  * and paged_prefill (which are these with window = 0), except that a query at position
  * p attends only to positions max(0, p - window + 1) .. p: the last `window` keys, the
  * mask that "PageAttention + FlashAttention golden combination" (section 4.1) builds.
- * window = 0 means no window; window < 0 is PA_ERR_INVALID_ARG.  Blocks wholly outside
- * the window are not read.  In split decode, a partition wholly before the window
- * still writes its partial (part_out 0, part_lse -inf), so paged_attention_reduce
- * merges the window's partials unchanged.
+ * window = 0 means no window; window < 0 is PA_ERR_INVALID_ARG.
+ * Blocks wholly before the window are not read, nor are their block-table entries
+ * used: for a sequence of ctx cached positions, entries of blocks that end at or before
+ * position ctx - window (decode) or ctx - Lq - window + 1 (paged prefill, the first
+ * row's window) may hold anything, so a caller may free those blocks.
+ * Split decode (partition_size > 0) computes only the partitions that hold a visible
+ * key, lo / P .. ceil(ctx / P) - 1 with lo = max(0, ctx - window); the partitions before
+ * them are left unwritten.  Merge with paged_attention_reduce_window and the same
+ * window, which starts at partition lo / P.
  */
 int paged_attention_decode_window(void* out, float* lse, float* part_out, float* part_lse,
                                   const void* q, const void* k_cache, const void* v_cache,
@@ -247,6 +252,12 @@ int varlen_causal_prefill_window(void* out, float* lse, const void* q, const voi
                                  int total_tokens, int max_seqlen, int num_q_heads,
                                  int num_kv_heads, int head_dim, float scale, int window,
                                  pa_dtype dtype, void* stream);
+
+int paged_attention_reduce_window(void* out, float* lse, const float* part_out,
+                                  const float* part_lse, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int head_dim,
+                                  int partition_size, int max_partitions, int window,
+                                  pa_dtype dtype, void* stream);
 
 int paged_prefill_window(void* out, float* lse, const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* block_tables,

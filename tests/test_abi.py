@@ -143,6 +143,8 @@ def test_window_validation(lib):
     assert lib.paged_prefill_window(p, p, p, p, p, p, p, p, 2, 100, 60, 32, 8, 128, 16, 8, 20, 128, 0.1, -1,
                                     1, None) == 1
     assert lib.varlen_causal_prefill_window(p, p, p, p, p, p, 0, 100, 60, 32, 8, 128, 0.1, 7, 1, None) == 0
+    assert lib.paged_attention_reduce_window(p, p, p, p, p, 2, 8, 128, 64, 4, -1, 1, None) == 1
+    assert lib.paged_attention_reduce_window(p, p, p, p, p, 0, 8, 128, 64, 4, 2048, 1, None) == 0
 
 
 def test_option(lib):

@@ -1,9 +1,12 @@
 """GPU parity of the sliding-window calls against the fp64 CPU oracle (C ABI).
 
 A query at position p keeps positions max(0, p - W + 1) .. p.  Decode is
-checked single-pass and split (the reduce merges the empty partials of the
-partitions wholly before the window), prefill and paged prefill on ragged
-sequences, each on the MFMA and the vector kernels.
+checked single-pass and split (partitions wholly before the window stay
+unwritten and the window-aware merge never reads them: they are filled with
+NaN beforehand), prefill and paged prefill on ragged sequences, each on the
+MFMA and the vector kernels; blocks before the window may be freed (table
+entries -1, their pool rows NaN); and the sliding-window decode workload
+(64 sequences of 1024..16384 positions, window 2048) at full size.
 """
 import numpy as np
 import pytest
@@ -17,18 +20,43 @@ from tests.gpu_util import assert_parity, to_dev, to_host_f64
 pytestmark = pytest.mark.gpu
 
 
-def decode_window(case, ps, window):
-    q, kc, vc = to_dev(case.q), to_dev(case.k_cache), to_dev(case.v_cache)
-    bt, cl = to_dev(case.block_tables), to_dev(case.context_lens)
+def decode_window(case, ps, window, tables=None, k_cache=None, v_cache=None, partials=False):
+    q = to_dev(case.q)
+    kc = to_dev(case.k_cache if k_cache is None else k_cache)
+    vc = to_dev(case.v_cache if v_cache is None else v_cache)
+    bt, cl = to_dev(case.block_tables if tables is None else tables), to_dev(case.context_lens)
     if case.slot_mapping.size:
         ops.paged_kv_write(to_dev(case.k_new), to_dev(case.v_new), kc, vc, to_dev(case.slot_mapping))
     if ps:
-        po, pl = ops.paged_attention_decode(q, kc, vc, bt, cl, case.max_context_len, case.scale, ps, window=window)
-        out, lse = ops.paged_attention_reduce(po, pl, cl, ps, out_dtype=q.dtype)
+        B, Hq, d = case.q.shape
+        P = ops.num_partitions(case.max_context_len, ps)
+        po = torch.full((B, Hq, P, d), float("nan"), dtype=torch.float32, device=q.device)
+        pl = torch.full((B, Hq, P), float("nan"), dtype=torch.float32, device=q.device)
+        ops.paged_attention_decode(q, kc, vc, bt, cl, case.max_context_len, case.scale, ps, part_out=po,
+                                   part_lse=pl, window=window)
+        out, lse = ops.paged_attention_reduce(po, pl, cl, ps, out_dtype=q.dtype, window=window)
     else:
         out, lse = ops.paged_attention_decode(q, kc, vc, bt, cl, case.max_context_len, case.scale, window=window)
     torch.cuda.synchronize()
+    if partials:
+        return to_host_f64(out), to_host_f64(lse), to_host_f64(po), to_host_f64(pl)
     return to_host_f64(out), to_host_f64(lse)
+
+
+def freed_before_window(case, first_keys):
+    """Tables with the blocks ending at or before each sequence's first visible
+    key unallocated (-1), and a pool whose freed blocks hold NaN."""
+    bs = case.spec.block_size
+    tables = case.block_tables.copy()
+    kc, vc = case.k_cache.copy(), case.v_cache.copy()
+    nanv = wl.nan_value(case.spec.dtype)
+    for b, k0 in enumerate(first_keys):
+        nfree = int(k0) // bs
+        ids = tables[b, :nfree]
+        ids = ids[ids >= 0]
+        kc[ids], vc[ids] = nanv, nanv
+        tables[b, :nfree] = -1
+    return tables, kc, vc
 
 
 def decode_oracle(case, window):
@@ -57,6 +85,34 @@ def test_window_decode(name, window):
     for ps in (0, 64):
         out, lse = decode_window(case, ps, window)
         assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"{name} window={window} ps={ps}")
+
+
+@pytest.mark.parametrize("window", [17, 100])
+def test_window_decode_split_partials_and_freed_blocks(window):
+    cfg, over = DECODE["bf16_g4_bs16"]
+    case = wl.make_case(cfg, **over)
+    ps, bs = 64, case.spec.block_size
+    ref_out, ref_lse = decode_oracle(case, window)
+    kc, vc = case.k_cache, case.v_cache
+    if case.slot_mapping.size:
+        kc, vc = oracle.kv_write(kc, vc, case.k_new, case.v_new, case.slot_mapping, bs)
+    ref_po, ref_pl = oracle.decode_partitions(case.q, kc, vc, case.block_tables, case.context_lens, bs, case.scale,
+                                              case.spec.dtype, ps, window=window)
+    out, lse, po, pl = decode_window(case, ps, window, partials=True)
+    assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"window={window} merged")
+    for b, n in enumerate(case.context_lens):
+        n = int(n)
+        first, live = max(0, n - window) // ps, -(-n // ps)
+        # partitions before the window and past the end are untouched
+        assert np.isnan(pl[b, :, :first]).all() and np.isnan(pl[b, :, live:]).all()
+        assert np.isnan(po[b, :, :first]).all() and np.isnan(po[b, :, live:]).all()
+        np.testing.assert_allclose(po[b, :, first:live], ref_po[b, :, first:live], rtol=0, atol=2e-2)
+        np.testing.assert_allclose(pl[b, :, first:live], ref_pl[b, :, first:live], rtol=0, atol=1e-3)
+    # blocks wholly before the window freed: same result, nothing of them read
+    tables, fk, fv = freed_before_window(case, [max(0, int(n) - window) for n in case.context_lens])
+    for p in (0, ps):
+        out, lse = decode_window(case, p, window, tables, fk, fv)
+        assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"freed window={window} ps={p}")
 
 
 def test_window_decode_vector_kernel():
@@ -120,3 +176,47 @@ def test_window_paged_prefill(name, window):
     ref_out, ref_lse = oracle.paged_prefill(case.q, okc, ovc, case.block_tables, case.cu_seqlens_q,
                                             case.context_lens, bs, case.scale, case.spec.dtype, window=window)
     assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, f"{name} window={window}")
+    # blocks before the first row's window freed (table -1, pool rows NaN), on
+    # the MFMA and the vector kernels
+    lq = np.diff(case.cu_seqlens_q)
+    tables, fk, fv = freed_before_window(case, np.maximum(case.context_lens - lq - window + 1, 0))
+    for vector in (False, True):
+        kc, vc = to_dev(fk), to_dev(fv)
+        ops.paged_kv_write(to_dev(case.k_new), to_dev(case.v_new), kc, vc, to_dev(case.slot_mapping))
+        try:
+            ops.set_force_vector_path(vector)
+            out, lse = ops.paged_prefill(to_dev(case.q), kc, vc, to_dev(tables), to_dev(case.cu_seqlens_q),
+                                         to_dev(case.context_lens), case.max_seqlen_q, case.max_context_len,
+                                         case.scale, window=window)
+            torch.cuda.synchronize()
+        finally:
+            ops.set_force_vector_path(False)
+        assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype,
+                      f"{name} freed window={window} vector={vector}")
+
+
+# ---------------------------------------------------------------------------
+# the sliding-window decode workload at full size (split as timed, and single
+# pass), oracle on a sample of sequences
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def window_workload():
+    case = wl.make_case(7)
+    bs = case.spec.block_size
+    kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
+    return case, kc, vc
+
+
+@pytest.mark.parametrize("ps", [256, 0])
+def test_window_decode_workload_full_size(window_workload, ps):
+    case, kc, vc = window_workload
+    W, bs = case.spec.window, case.spec.block_size
+    out, lse = decode_window(case, ps, W)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    lens = case.context_lens
+    # the shortest (whole history visible), the longest, and a spread between
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31, 47, 63})
+    for b in sample:
+        ro, rl = oracle.decode(case.q[b:b + 1], kc, vc, case.block_tables[b:b + 1], lens[b:b + 1], bs,
+                               case.scale, case.spec.dtype, window=W)
+        assert_parity(out[b:b + 1], lse[b:b + 1], ro, rl, case.spec.dtype, f"seq {b} ctx={int(lens[b])} ps={ps}")
