@@ -161,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // row's window start): tile slots below it load key kmin instead (masked),
   // so blocks wholly before the window are never touched and may be freed.
   const int kmin = win > 0 ? max(0, ks.pos0 + qw0 - win + 1) : 0;
+  const unsigned wlim = win > 0 ? static_cast<unsigned>(win) : 0x7fffffffu;   // visible: 0 <= pos - key < wlim
 
   // LDS-DMA of key tile kt: 2048 chunks (K then V); wave w issues slices
   // w, w+4, ..., each 64 lanes x 16 B.  Slice i holds rows 4(i%16) + lane/16 at
@@ -248,14 +249,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       // results to the vector ALU under the compiler's hazard tracking before
       // the inline-asm max reads them.
       float sv[4][4];
-      const int qrow = ks.pos0 + q0 + 16 * rg + c16;   // the row's position among the keys
+      // The row's position (among the keys) minus this lane's first key of the
+      // tile, kt*64 + 4j: key kt*64 + 4j + 16nt + i is visible iff
+      // 0 <= d - (16nt + i) < wlim, one unsigned compare per element.
+      const int d = ks.pos0 + q0 + 16 * rg + c16 - kt * kPN - 4 * j;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sv[nt][i] = sacc[nt][rg][i] * sl2;
-          const int key = kt * kPN + 16 * nt + 4 * j + i;
-          if (masked && (key > qrow || (win > 0 && key <= qrow - win))) sv[nt][i] = kNegInf;
+          if (masked && static_cast<unsigned>(d - (16 * nt + i)) >= wlim) sv[nt][i] = kNegInf;
         }
       float mx = vmax3(vmax3(sv[0][0], sv[0][1], sv[0][2]), vmax3(sv[0][3], sv[1][0], sv[1][1]),
                        vmax3(sv[1][2], sv[1][3], sv[2][0]));
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int p_first = ks.pos0 + q0, p_last = ks.pos0 + min(q0 + 31, sp.len - 1);
   const int kt_first = win > 0 ? max(0, p_first - win + 1) >> 6 : 0;
   const int kt_wfull = win > 0 ? (max(0, p_last - win + 1) + kPN - 1) >> 6 : 0;
-  const int kt_cfull = (p_first + 1) >> 6;   // tiles below are causally full
+  const int kt_cfull = wave_live ? (p_first + 1) >> 6 : 0;   // tiles below are causally full
   const int kt_last = wave_live ? p_last >> 6 : -1;
   const int kt0 = kmin >> 6;
   load_ids(kt0, ids_cur);
@@ -361,9 +364,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       issue(kt + 1, kvbuf + ((kt + 1) & 1) * 2048);
       if (kt + 2 < nkt) load_ids(kt + 2, ids_next);
     }
-    if (kt < kt_first || kt > kt_last) continue;   // nothing visible to this wave
+    // (kt_wfull >= kt_first and kt_cfull <= kt_last + 1, so the unmasked range
+    // lies inside the visible one; this form of the test also keeps the loop
+    // within the register budget, which a skip-first form does not)
     if (kt >= kt_wfull && kt < kt_cfull) tile(kt, false);
-    else tile(kt, true);
+    else if (kt >= kt_first && kt <= kt_last) tile(kt, true);
   }
 
   uint16_t* out = static_cast<uint16_t*>(a.out);

@@ -11,7 +11,11 @@ Inputs are resident in HBM before timing.  R independent copies of the pools,
 tables and queries are rotated so the 256 MB Infinity Cache cannot serve one
 step's KV from the previous step.  The varlen causal prefill on the
 Llama-3-8B varlen workload (16 sequences, lengths uniform in [64, 2048]) is
-timed as a secondary figure (TFLOP/s over unmasked query-key pairs).
+timed as a secondary figure (TFLOP/s over unmasked query-key pairs), and so
+are the chunked paged prefill (16 sequences, cached prefix 0..3072, chunk
+128..1024) and, under a 2048-key sliding window, the split decode of 64
+sequences of 1024..16384 positions (GB/s over the window's KV bytes) and the
+chunked paged prefill (TFLOP/s over the window's query-key pairs).
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -77,6 +81,7 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=3, help="independent input copies rotated per step")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-window", action="store_true", help="skip the sliding-window figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -226,6 +231,7 @@ def main(argv=None):
 
     # ----------------------------------------------------------------- prefill
     prefill = None
+    window_prefill = None
     if not args.no_prefill:
         t0 = time.perf_counter()
         pc = wl.make_case(3)
@@ -313,7 +319,103 @@ def main(argv=None):
                          "tokens_per_s": round(cc.total_q / (cms * 1e-3), 1)}
         prefill["paged_prefill"] = paged_prefill
         log(f"paged prefill {cms * 1e3:.1f} us -> {ctf:.1f} TFLOP/s")
+
+        # the same chunks under a sliding window of 2048 keys: row at position p
+        # sees min(p + 1, 2048) keys
+        if not args.no_window:
+            PW = 2048
+            vis = np.concatenate([np.minimum(np.arange(p0, p0 + n) + 1, PW) for p0, n in zip(pre, lq)])
+            wflops = 4.0 * cc.spec.head_dim * cc.spec.num_q_heads * float(vis.sum())
+
+            def chunked_w():
+                ops.paged_prefill(cq, ckc, cvc, cbt, ccu, ccl, cc.max_seqlen_q, cc.max_context_len, cc.scale,
+                                  out=cout, lse=clse, window=PW)
+            for _ in range(3):
+                chunked_w()
+            torch.cuda.synchronize()
+            pa_.record(stream)
+            for _ in range(args.prefill_iters):
+                chunked_w()
+            pb_.record(stream)
+            torch.cuda.synchronize()
+            wpms = pa_.elapsed_time(pb_) / args.prefill_iters
+            wtf = wflops / (wpms * 1e-3) / 1e12
+            window_prefill = {"workload": cc.spec.name, "window": PW, "kernel_avg_us": round(wpms * 1e3, 1),
+                              "tflops": round(wtf, 1),
+                              "roofline": {"bound": "mfma", "achieved": round(wtf, 1), "peak": BF16_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(wtf / BF16_PEAK_TFLOPS, 4),
+                                           "traffic": None,
+                                           "kernel": "prefill_mfma_kernel<NW=4, paged> (paged_prefill_window)",
+                                           "algorithmic_flops_per_launch": wflops},
+                              "flops_vs_no_window": round(wflops / cflops, 4)}
+            log(f"windowed paged prefill {wpms * 1e3:.1f} us -> {wtf:.1f} TFLOP/s")
         del ckc, cvc, cq, cout
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------- sliding window
+    window = None
+    if not args.no_window:
+        t0 = time.perf_counter()
+        wc = wl.make_case(7)
+        W, wps = wc.spec.window, wc.spec.partition_size
+        wB, wHq, wHkv, wd = wc.spec.batch, wc.spec.num_q_heads, wc.spec.num_kv_heads, wc.spec.head_dim
+        log(f"window workload generated in {time.perf_counter() - t0:.1f}s: NB={wc.num_blocks}")
+        # algorithmic bytes: K and V of the visible keys, min(ctx, W) per sequence
+        wvis = np.minimum(wc.context_lens.astype(np.int64), W)
+        wbytes = int(wvis.sum()) * wHkv * 2 * wd * 2
+        wP = ops.num_partitions(wc.max_context_len, wps)
+        wcopies = []
+        for _ in range(2):   # two pool copies: the window's KV of one launch exceeds the Infinity Cache anyway
+            c = dict(q=up(wc.q), kc=up(wc.k_cache), vc=up(wc.v_cache), bt=up(wc.block_tables),
+                     cl=up(wc.context_lens),
+                     po=torch.empty((wB, wHq, wP, wd), dtype=torch.float32, device=dev),
+                     pl=torch.empty((wB, wHq, wP), dtype=torch.float32, device=dev),
+                     out=torch.empty((wB, wHq, wd), dtype=torch.bfloat16, device=dev),
+                     lse=torch.empty((wB, wHq), dtype=torch.float32, device=dev))
+            ops.paged_kv_write(up(wc.k_new), up(wc.v_new), c["kc"], c["vc"], up(wc.slot_mapping))
+            wcopies.append(c)
+
+        def wdecode(c):
+            ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], wc.max_context_len, wc.scale,
+                                       wps, part_out=c["po"], part_lse=c["pl"], window=W)
+
+        def wstep(c):
+            wdecode(c)
+            ops.paged_attention_reduce(c["po"], c["pl"], c["cl"], wps, out=c["out"], lse=c["lse"], window=W)
+
+        def timed(fn, n_groups):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n_groups)]
+            torch.cuda.synchronize()
+            for gi in range(n_groups):
+                evs[gi][0].record(stream)
+                for k in range(group):
+                    fn(wcopies[(gi * group + k) % len(wcopies)])
+                evs[gi][1].record(stream)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) / group for a, b in evs]
+        for i in range(10):
+            wstep(wcopies[i % 2])
+        wg = max(1, args.steps // group)
+        wdec_ms = timed(wdecode, wg)
+        wstep_ms = timed(wstep, wg)
+        wavg = float(np.mean(wdec_ms))
+        wgbs = wbytes / (wavg * 1e-3) / 1e9
+        window = {"workload": wc.spec.name, "window": W, "partition_size": wps,
+                  "sum_context": int(wc.context_lens.sum()), "visible_keys": int(wvis.sum()),
+                  "kv_bytes_per_step": wbytes,
+                  "step_us": round(float(np.mean(wstep_ms)) * 1e3, 2),
+                  "step_gbs": round(wbytes / (float(np.mean(wstep_ms)) * 1e-3) / 1e9, 1),
+                  "roofline": {"bound": "hbm", "achieved": round(wgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(wgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                               "kernel": "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode_window)",
+                               "kernel_avg_us": round(wavg * 1e3, 2),
+                               "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
+                               "algorithmic_bytes_per_launch": wbytes},
+                  "decode_tokens_per_s": round(wB / (float(np.mean(wstep_ms)) * 1e-3), 1),
+                  "paged_prefill": window_prefill}
+        log(f"window decode kernel {wavg * 1e3:.1f} us -> {wgbs:.0f} GB/s; step {np.mean(wstep_ms) * 1e3:.1f} us")
+        del wcopies
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline
@@ -369,6 +471,7 @@ def main(argv=None):
         "stream_ceiling": stream_ceiling,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "window": window,
     }
     print(json.dumps(line), flush=True)
 
