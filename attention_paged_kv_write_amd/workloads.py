@@ -32,8 +32,10 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+E4M3 = "e4m3"                 # OCP FP8 E4M3 codes stored as uint8
 
 BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN_CODE = np.uint8(0x7F)   # the E4M3 NaN code: unwritten FP8 pool slots
 
 
 # --------------------------------------------------------------------------
@@ -105,6 +107,9 @@ class DecodeSpec:
     pool_copies: int = 1                  # bench: independent copies (defeat MALL)
     window: int = 0                       # sliding window of keys (0 = none)
     free_before_window: bool = False      # blocks wholly before the window are unallocated (-1)
+    kv_dtype: Optional[str] = None        # "e4m3": FP8 pools, every position written through the FP8 write
+    k_scale: float = 1.0                  # FP8 pools: per-pool scales (value = code * scale)
+    v_scale: float = 1.0
 
 
 @dataclass
@@ -119,6 +124,8 @@ class DecodeCase:
     v_new: np.ndarray
     slot_mapping: np.ndarray   # [T_new] int32
     scale: float
+    k_scale: float = 1.0       # FP8 pools only
+    v_scale: float = 1.0
 
     @property
     def max_context_len(self) -> int:
@@ -179,6 +186,9 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
             tables[b, f:n] = perm[cursor:cursor + n - f]
             cursor += n - f
 
+    if spec.kv_dtype == E4M3:
+        return _fp8_decode_case(spec, rng, ctx, tables, first_blk, NB)
+
     # 3. history K/V: iid draws over the whole pool, then NaN where unused
     shape = (NB, Hkv, bs, d)
     k_cache = _draw(rng, shape, spec.dtype, "normal")
@@ -216,6 +226,29 @@ def make_decode_case(spec: DecodeSpec, seed: int) -> DecodeCase:
     return DecodeCase(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache,
                       block_tables=tables, context_lens=ctx, k_new=k_new,
                       v_new=v_new, slot_mapping=slots, scale=1.0 / math.sqrt(d))
+
+
+def _fp8_decode_case(spec, rng, ctx, tables, first_blk, NB) -> DecodeCase:
+    """FP8 pools start as all-NaN codes; every allocated position of every
+    sequence (history and the new token) arrives as a bf16/f32 row through
+    the FP8 cache write, whose slots are returned.  Draws after the block
+    permutation: q, then the rows' k, then their v."""
+    B, Hq, Hkv, d, bs = (spec.batch, spec.num_q_heads, spec.num_kv_heads,
+                         spec.head_dim, spec.block_size)
+    k_cache = np.full((NB, Hkv, bs, d), E4M3_NAN_CODE, dtype=np.uint8)
+    v_cache = k_cache.copy()
+    q = _draw(rng, (B, Hq, d), spec.dtype, "normal")
+    slots = []
+    for b in range(B):
+        for p in range(int(first_blk[b]) * bs, int(ctx[b])):
+            slots.append(int(tables[b, p // bs]) * bs + p % bs)
+    slots = np.asarray(slots, dtype=np.int32)
+    k_new = _draw(rng, (len(slots), Hkv, d), spec.dtype, "normal")
+    v_new = _draw(rng, (len(slots), Hkv, d), spec.dtype, spec.v_dist)
+    return DecodeCase(spec=spec, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=tables,
+                      context_lens=ctx, k_new=k_new, v_new=v_new, slot_mapping=slots,
+                      scale=1.0 / math.sqrt(d), k_scale=float(np.float32(spec.k_scale)),
+                      v_scale=float(np.float32(spec.v_scale)))
 
 
 # --------------------------------------------------------------------------
@@ -451,6 +484,14 @@ LLAMA3_8B_CHUNKED_PREFILL = PagedPrefillSpec(
     num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
     prefix_min=0, prefix_max=3072, chunk_min=128, chunk_max=1024)
 
+# The Llama-3-8B decode workload over an FP8 (E4M3) cache: same shapes and
+# context lengths as workload 2; the whole history is written through the FP8
+# cache write with per-pool scales 6/448 (K) and 5/448 (V), about the largest
+# magnitude of the N(0,1) rows over 448, so a few outliers saturate.
+LLAMA3_8B_DECODE_FP8 = replace(
+    LLAMA3_8B_DECODE, name="llama3_8b_paged_decode_fp8_e4m3", kv_dtype=E4M3,
+    k_scale=6.0 / 448.0, v_scale=5.0 / 448.0)
+
 CONFIGS = {
     1: TINY_DECODE_F32,
     2: LLAMA3_8B_DECODE,
@@ -459,6 +500,7 @@ CONFIGS = {
     5: LONG_CONTEXT_SPLIT_DECODE,
     6: LLAMA3_8B_CHUNKED_PREFILL,
     7: LLAMA3_8B_WINDOW_DECODE,
+    8: LLAMA3_8B_DECODE_FP8,
 }
 
 
@@ -467,7 +509,7 @@ def seed_for(config_index: int) -> int:
 
 
 def make_case(config_index: int, seed: Optional[int] = None, **overrides):
-    """Build workload ``config_index`` (1..7), optionally shrunk by overrides."""
+    """Build workload ``config_index`` (1..8), optionally shrunk by overrides."""
     spec = CONFIGS[config_index]
     if overrides:
         spec = replace(spec, **overrides)

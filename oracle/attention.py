@@ -47,12 +47,17 @@ import math
 
 import numpy as np
 
+from .e4m3 import E4M3, e4m3_value
+
 F32 = "f32"
 BF16 = "bf16"
 
 
 def upcast(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact widening to float64 (bf16 given as uint16 bit patterns)."""
+    """Exact widening to float64 (bf16 given as uint16 bit patterns, E4M3
+    as uint8 codes, widened to their unscaled values)."""
+    if dtype == E4M3:
+        return e4m3_value(x)
     if dtype == BF16:
         bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
@@ -147,16 +152,24 @@ def group_of(h, num_q_heads, num_kv_heads):
 # ---------------------------------------------------------------------------
 # decode: each sequence's query against its paged history
 # ---------------------------------------------------------------------------
+def kv_rows(rows, dtype, kv_dtype, scale):
+    """Gathered cache rows as float64: widened in the input dtype, or for an
+    E4M3 cache the code values times the pool's fp32 scale."""
+    if kv_dtype is None:
+        return upcast(rows, dtype)
+    return upcast(rows, kv_dtype) * float(np.float32(scale))
+
+
 def decode_one(q, k_cache, v_cache, block_tables, context_lens, block_size,
-               scale, dtype, b, h, positions=None):
+               scale, dtype, b, h, positions=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Output and lse of query head h of sequence b (optionally a position range)."""
     Hq = q.shape[1]
     Hkv = k_cache.shape[1]
     ctx = int(context_lens[b])
     g = group_of(h, Hq, Hkv)
     # gather from the KV head's slice of the pool only (a view, same bytes)
-    K = upcast(gather(k_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype)[:, 0, :]
-    V = upcast(gather(v_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype)[:, 0, :]
+    K = kv_rows(gather(k_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype, kv_dtype, k_scale)[:, 0, :]
+    V = kv_rows(gather(v_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype, kv_dtype, v_scale)[:, 0, :]
     if positions is not None:
         lo, hi = positions
         K, V = K[lo:hi], V[lo:hi]
@@ -171,14 +184,15 @@ def window_start(pos, window):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
-           dtype, return_probs=False, window=0):
+           dtype, return_probs=False, window=0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """PagedAttention decode for a batch: out [B, H_q, d] float64, lse [B, H_q].
 
     Each new token attends over its sequence's whole history, gathered block
     by block through the table ("PageAttention + FlashAttention golden
     combination", section 2.1; LLaMA page, section 3.2), with query heads
     sharing KV heads in groups (LLaMA page, section 2.1).  With a sliding
-    window only the last `window` positions are seen.
+    window only the last `window` positions are seen.  ``kv_dtype`` = E4M3:
+    the pools hold E4M3 codes, read as code value times k_scale / v_scale.
     """
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
@@ -188,8 +202,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
     for b in range(B):
         ctx = int(context_lens[b])
         lo = window_start(ctx - 1, window) if ctx > 0 else 0
-        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size, lo), dtype)
-        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size, lo), dtype)
+        Kall = kv_rows(gather(k_cache, block_tables[b], ctx, block_size, lo), dtype, kv_dtype, k_scale)
+        Vall = kv_rows(gather(v_cache, block_tables[b], ctx, block_size, lo), dtype, kv_dtype, v_scale)
         for h in range(Hq):
             g = group_of(h, Hq, Hkv)
             o, l, p = attend(upcast(q[b, h], dtype), Kall[:, g, :], Vall[:, g, :], scale)
@@ -209,7 +223,7 @@ def num_partitions(max_context_len, partition_size):
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
                       block_size, scale, dtype, partition_size,
-                      max_partitions=None, window=0):
+                      max_partitions=None, window=0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Attention restricted to each partition of positions.
 
     Returns part_out [B, H_q, P, d] and part_lse [B, H_q, P]; a partition that
@@ -225,8 +239,8 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
         ctx = int(context_lens[b])
         wlo = window_start(ctx - 1, window) if ctx > 0 else 0
         # Kall[i] holds position wlo + i
-        Kall = upcast(gather(k_cache, block_tables[b], ctx, block_size, wlo), dtype)
-        Vall = upcast(gather(v_cache, block_tables[b], ctx, block_size, wlo), dtype)
+        Kall = kv_rows(gather(k_cache, block_tables[b], ctx, block_size, wlo), dtype, kv_dtype, k_scale)
+        Vall = kv_rows(gather(v_cache, block_tables[b], ctx, block_size, wlo), dtype, kv_dtype, v_scale)
         for i in range(P):
             lo, hi = max(i * partition_size, wlo), min((i + 1) * partition_size, ctx)
             if lo >= hi:
