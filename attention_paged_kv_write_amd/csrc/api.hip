@@ -86,6 +86,105 @@ int paged_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
   return launch_status(pa::launch_kv_write(a, static_cast<hipStream_t>(stream)), "paged_kv_write");
 }
 
+int paged_kv_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                       const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, const float* k_scale, const float* v_scale,
+                       pa_dtype dtype, void* stream) {
+  const char* fn = "paged_kv_write_fp8";
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", fn);
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_blocks * block_size exceeds int32 slots", fn);
+  if (head_dim % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 16", fn);
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::KvWriteFp8Args a;
+  a.k = k;
+  a.v = v;
+  a.k_cache = static_cast<pa::u32x4*>(k_cache);
+  a.v_cache = static_cast<pa::u32x4*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_chunks = head_dim / 16;
+  a.row_chunks = num_kv_heads * a.head_chunks;
+  a.block_size = block_size;
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  return launch_status(pa::launch_kv_write_fp8(a, dt, static_cast<hipStream_t>(stream)), fn);
+}
+
+int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                               int partition_size, int max_context_len, float scale, const float* k_scale,
+                               const float* v_scale, int window, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode_fp8";
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be 0 or a multiple of block_size", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
+  if (dtype != PA_BF16 || head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: bf16 queries with head_dim 128 only", fn);
+  if (!(block_size == 16 || block_size == 32 || block_size == 64))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  const int G = num_q_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, G);
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !k_scale || !v_scale)
+    return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
+  int num_parts = 1;
+  if (partition_size > 0) {
+    if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
+    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
+  } else if (!out || !lse) {
+    return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
+  }
+  pa::DecodeArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.num_partitions = num_parts;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * pa::kLog2e;
+  a.flat_units = 0;
+  a.window = window;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_status(pa::launch_decode_fp8(a, head_dim, static_cast<hipStream_t>(stream)), fn);
+}
+
 int paged_attention_decode(void* out, float* lse, float* part_out, float* part_lse, const void* q,
                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
                            const int32_t* context_lens, int num_seqs, int num_q_heads,
@@ -158,6 +257,8 @@ int paged_attention_decode_window(void* out, float* lse, float* part_out, float*
   a.scale_log2 = scale * pa::kLog2e;
   a.flat_units = 0;
   a.window = window;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
   const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s)

@@ -393,6 +393,63 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
 #endif
 }
 
+// FP8 tile, first step: this lane's 32 K codes and 32 V codes (two 16-byte
+// reads each) from its LDS ring slot, then wait for them.
+__device__ __forceinline__ void lds_read_fp8_tile(u32x4* k8, u32x4* v8, const uint32_t* k_addr,
+                                                  const uint32_t* v_addr, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k8[0]), "=&v"(k8[1]), "=&v"(v8[0]), "=&v"(v8[1])
+      : "v"(k_addr[0] + off), "v"(k_addr[1] + off), "v"(v_addr[0] + off), "v"(v_addr[1] + off)
+      : "memory");
+#endif
+}
+
+// FP8 tile, second step: store this lane's 32 converted V values (bf16) into
+// the wave's staging tile, wait, then the eight transposed reads of V^T.
+__device__ __forceinline__ void lds_stage_v_read_tr(const u32x4* vb, const uint32_t* st_addr, u32x2* vt,
+                                                    const uint32_t* v_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "ds_write_b128 %8, %12\n\t"
+      "ds_write_b128 %9, %13\n\t"
+      "ds_write_b128 %10, %14\n\t"
+      "ds_write_b128 %11, %15\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %20\n\t"
+      "ds_read_b64_tr_b16 %5, %21\n\t"
+      "ds_read_b64_tr_b16 %6, %22\n\t"
+      "ds_read_b64_tr_b16 %7, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vt[0]), "=&v"(vt[1]), "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]),
+        "=&v"(vt[6]), "=&v"(vt[7])
+      : "v"(st_addr[0]), "v"(st_addr[1]), "v"(st_addr[2]), "v"(st_addr[3]), "v"(vb[0]), "v"(vb[1]),
+        "v"(vb[2]), "v"(vb[3]), "v"(v_addr[0]), "v"(v_addr[1]), "v"(v_addr[2]), "v"(v_addr[3]),
+        "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7])
+      : "memory");
+#endif
+}
+
+// Eight E4M3 codes (two dwords) -> eight bf16 (exact: every E4M3 value is a
+// bf16 value), low byte first.  The convert's scale operand is 1.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel: bf16, head_dim 128, block_size a multiple of 16
 // ---------------------------------------------------------------------------
@@ -419,17 +476,32 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
 // row-major with XOR-swizzled 16-byte chunks: K chunk q of token t at q ^ t
 // (conflict-free lane-linear b128 reads), V at q ^ 2*(t%8) (the eight tokens a
 // transposed read touches spread over all 64 banks).
-template <int G, int BS, int W>
+//
+// KV8: the pools hold E4M3 codes (half the bytes).  A ring slot holds the K
+// and V tiles as codes (2 KB each, row-major, chunk q of token t at
+// q ^ (t/2): conflict-free 16-byte reads of 128-byte rows).  K: the dot
+// product's dims are taken in a permuted order so that MFMA c, lane (j, c16)
+// uses dims 32j + 8c .. +7 of token c16 (Q is loaded in the same order):
+// each lane's 32 dims are one contiguous 32-byte run, read with two
+// ds_read_b128 and converted to bf16 operands.  V: lane l converts dims
+// 32(l%4) .. +31 of token l/4 to bf16 into a per-wave staging tile laid out
+// like the bf16 V tile, which the transposed reads then use unchanged.  The
+// K scale multiplies the softmax scale, the V scale the output.
+template <int G, int BS, int W, bool KV8>
 __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int RC = D * 2 / 16;   // 16-byte chunks per row (16)
+  constexpr int RC = D * 2 / 16;   // 16-byte chunks per bf16 row (16)
+  constexpr int RC8 = D / 16;      // 16-byte chunks per E4M3 row (8)
   constexpr int TPB = BS / 16;     // 16-token tiles per block
   typedef short short4v __attribute__((ext_vector_type(4)));
 
   // LDS ring, per slot and wave: K tile (4 KB, MFMA A layout, lane-linear)
-  // then V tile (4 KB, row-major, chunk-swizzled)
-  constexpr int kSlotBytes = 512 * 16;
-  __shared__ __attribute__((aligned(16))) u32x4 ring[W][2][512];
+  // then V tile (4 KB, row-major, chunk-swizzled); KV8: 2 KB each, plus the
+  // bf16 V staging tile
+  constexpr int kSlotChunks = KV8 ? 256 : 512;
+  constexpr int kSlotBytes = kSlotChunks * 16;
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][2][kSlotChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 stage[KV8 ? W : 1][KV8 ? 256 : 1];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
   __shared__ float sm_acc[W > 1 ? W : 1][G][D];
@@ -462,7 +534,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (c16 < G) w = qc[row * RC + 4 * c + j];
+      if (c16 < G) w = qc[row * RC + (KV8 ? 4 * j + c : 4 * c + j)];
       qf[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -508,12 +580,34 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   // K row t, dim chunk q is stored at chunk q ^ t of the slot's row t; the MFMA
   // A operand of instruction c wants row c16, chunk 4c + j
   uint32_t k_addr[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) k_addr[c] = lds_addr(&ring[wave][0][16 * c16 + ((4 * c + j) ^ c16)]);
   uint32_t v_addr[8];
+  uint32_t k8_addr[2], v8_addr[2], st_addr[4];   // KV8 only
+  if constexpr (!KV8) {
 #pragma unroll
-  for (int dn = 0; dn < 8; ++dn)
-    v_addr[dn] = lds_addr(&ring[wave][0][256]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
+    for (int c = 0; c < 4; ++c) k_addr[c] = lds_addr(&ring[wave][0][16 * c16 + ((4 * c + j) ^ c16)]);
+#pragma unroll
+    for (int dn = 0; dn < 8; ++dn)
+      v_addr[dn] = lds_addr(&ring[wave][0][256]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
+  } else {
+    // K codes: token c16, chunks 2j and 2j+1 (stored at q ^ (c16/2))
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k8_addr[e] = lds_addr(&ring[wave][0][8 * c16 + ((2 * j + e) ^ (c16 >> 1))]);
+    // V codes to convert: token lane/4, chunks 2(lane%4) and +1
+    const int vtok = lane >> 2, vq = 2 * (lane & 3);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      v8_addr[e] = lds_addr(&ring[wave][0][128 + 8 * vtok + ((vq + e) ^ (vtok >> 1))]);
+    // their bf16 chunks 4(lane%4) + u in the staging tile, swizzled like the bf16 V tile
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st_addr[u] = lds_addr(&stage[wave][16 * vtok + ((4 * (lane & 3) + u) ^ (2 * (vtok & 7)))]);
+#pragma unroll
+    for (int dn = 0; dn < 8; ++dn)
+      v_addr[dn] = lds_addr(&stage[wave][0]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
+  }
+  // E4M3 scales (device scalars): K folds into the softmax scale, V into the output
+  const float sl2 = KV8 ? a.scale_log2 * a.k_scale[0] : a.scale_log2;
+  const float vsc = KV8 ? a.v_scale[0] : 1.f;
 
   for (int w0 = 0; w0 < n_blocks; w0 += 64) {
     if (w0 > 0) ids = load_ids(w0);
@@ -536,6 +630,19 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
     auto fetch = [&](int n, int slot) {
       int pos0, lim, phys;
       tile_span(n, pos0, lim, phys);
+      if constexpr (KV8) {
+        // 16 rows x 8 chunks per tile and pool: two loads of 64 chunks each;
+        // physical chunk lane%8 of row 8i + lane/8 holds chunk (lane%8) ^ (row/2)
+        const size_t base8 = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC8;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int tok = 8 * i + (lane >> 3);
+          const int q = (lane & 7) ^ (tok >> 1);
+          global_to_lds16<PA_DECODE_AUX>(kc + base8 + tok * RC8 + q, &ring[wave][slot][64 * i]);
+          global_to_lds16<PA_DECODE_AUX>(vc + base8 + tok * RC8 + q, &ring[wave][slot][128 + 64 * i]);
+        }
+        return;
+      }
       const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -557,7 +664,18 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       const uint32_t off = slot * kSlotBytes;
       u32x4 kw[4];
       u32x2 vt[8];
-      lds_read_decode_tile(kw, vt, k_addr, v_addr, off);
+      if constexpr (!KV8) {
+        lds_read_decode_tile(kw, vt, k_addr, v_addr, off);
+      } else {
+        u32x4 k8[2], v8[2];
+        lds_read_fp8_tile(k8, v8, k8_addr, v8_addr, off);
+        u32x4 vb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vb[u] = e4m3x8_to_bf16(v8[u >> 1][2 * (u & 1)], v8[u >> 1][2 * (u & 1) + 1]);
+        lds_stage_v_read_tr(vb, st_addr, vt, v_addr);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kw[c] = e4m3x8_to_bf16(k8[c >> 1][2 * (c & 1)], k8[c >> 1][2 * (c & 1) + 1]);
+      }
       floatx4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -567,7 +685,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = pos0 + 4 * j + i;
-        s[i] = (pos < lim && pos >= r.lo) ? st[i] * a.scale_log2 : kNegInf;
+        s[i] = (pos < lim && pos >= r.lo) ? st[i] * sl2 : kNegInf;
       }
       const float mx = quarter_max(vmax3(vmax3(s[0], s[1], s[2]), s[3], s[3]));
       // lazy rescale: the running max moves (with l and O) only when some
@@ -601,7 +719,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
     };
 
     // Two-slot ring: tile n+1's loads are issued before tile n is computed;
-    // the wait then lets exactly those 8 loads stay in flight (none after the
+    // the wait then lets exactly those 8 loads (4 for E4M3) stay in flight (none after the
     // last tile, so no tile is fetched twice).  The compiler cannot count
     // LDS-DMA completions, so the waits are explicit.
     fetch(0, 0);
@@ -609,7 +727,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       const int slot = n & 1;
       if (n + 1 < nt) {
         fetch(n + 1, slot ^ 1);
-        wait_vmcnt<8>();
+        wait_vmcnt<KV8 ? 4 : 8>();
       } else {
         wait_vmcnt<0>();
       }
@@ -619,7 +737,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   l = across_rows(l, OpSum());
   if constexpr (W == 1) {
     if (c16 >= G) return;
-    const float inv = 1.f / l;
+    const float inv = vsc / l;
     const float lse = (m + __log2f(l)) * kLn2;
     const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
     if (a.partition_size > 0) {
@@ -644,7 +762,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
       for (int dn = 0; dn < 8; ++dn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm_acc[wave][c16][16 * dn + 4 * j + i] = oacc[dn][i];
+        for (int i = 0; i < 4; ++i) sm_acc[wave][c16][16 * dn + 4 * j + i] = oacc[dn][i] * vsc;
       if (j == 0) {
         sm_m[wave][c16] = m;
         sm_l[wave][c16] = l;
@@ -660,7 +778,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int G, int BS>
+template <int G, int BS, bool KV8>
 hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.partition_size > 0) {
     // flat grid of balanced units (one per KV head and live partition, in the
@@ -675,18 +793,18 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
     const dim3 fg = f.flat_units ? dim3(static_cast<unsigned>(nwg)) : grid;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1>), fg, dim3(64), 0, s, f);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, KV8>), fg, dim3(64), 0, s, f);
   } else
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, KV8>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool KV8 = false>
 hipError_t launch_mfma_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   switch (a.block_size) {
-    case 16: return launch_mfma_gb<G, 16>(a, grid, s);
-    case 32: return launch_mfma_gb<G, 32>(a, grid, s);
-    case 64: return launch_mfma_gb<G, 64>(a, grid, s);
+    case 16: return launch_mfma_gb<G, 16, KV8>(a, grid, s);
+    case 32: return launch_mfma_gb<G, 32, KV8>(a, grid, s);
+    case 64: return launch_mfma_gb<G, 64, KV8>(a, grid, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -728,6 +846,22 @@ hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_
     if (head_dim == 128) return launch_generic_d<false, 128>(a, G, grid, s);
   }
   return hipErrorNotSupported;
+}
+
+// E4M3 pools: the MFMA kernel only (bf16 queries, head_dim 128, block_size a
+// multiple of 16, group 1, 2, 4 or 8).
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, hipStream_t s) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const dim3 grid(static_cast<unsigned>(a.num_kv_heads), static_cast<unsigned>(a.num_seqs),
+                  static_cast<unsigned>(a.num_partitions));
+  if (head_dim != 128 || a.block_size % 16 != 0) return hipErrorNotSupported;
+  switch (G) {
+    case 1: return launch_mfma_g<1, true>(a, grid, s);
+    case 2: return launch_mfma_g<2, true>(a, grid, s);
+    case 4: return launch_mfma_g<4, true>(a, grid, s);
+    case 8: return launch_mfma_g<8, true>(a, grid, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 // Exposed for tests of the vector-ALU kernel on shapes the MFMA kernel owns.

@@ -21,6 +21,23 @@ struct KvWriteArgs {
   int64_t num_slots;     // NB * bs
 };
 
+// paged_kv_write into E4M3 pools: 16 codes (one 16-byte chunk) per thread.
+struct KvWriteFp8Args {
+  const void* k;         // [T, H_kv, d] bf16 or f32
+  const void* v;
+  u32x4* k_cache;        // [NB, H_kv, bs, d] E4M3 codes as 16-byte chunks
+  u32x4* v_cache;
+  const int32_t* slot_mapping;
+  const float* k_scale;  // device scalars
+  const float* v_scale;
+  int num_tokens;
+  int num_kv_heads;
+  int head_chunks;       // d / 16
+  int row_chunks;        // H_kv * head_chunks
+  int block_size;
+  int64_t num_slots;
+};
+
 struct DecodeArgs {
   void* out;             // [B, H_q, d] (T)        when partition_size == 0
   float* lse;            // [B, H_q]               when partition_size == 0
@@ -43,6 +60,8 @@ struct DecodeArgs {
   float scale_log2;      // scale * log2(e)
   int flat_units;        // split-KV MFMA kernel: 1-D grid of balanced work units
   int window;            // sliding window in keys (0 = none)
+  const float* k_scale;  // E4M3 pools only: device scalars, value = code * scale
+  const float* v_scale;
 };
 
 struct ReduceArgs {
@@ -85,6 +104,8 @@ struct PrefillArgs {
 enum class DType { F32 = 0, BF16 = 1 };
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, hipStream_t stream);
 
 // Returns hipErrorNotSupported when no kernel instance covers the shape.
 hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);

@@ -34,6 +34,76 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   pool[dst] = __builtin_nontemporal_load(in + src);
 }
 
+// E4M3 pools: every thread writes one 16-byte chunk of codes (16 elements of
+// a row).  A code is the E4M3 value nearest to x / scale (one IEEE fp32
+// division; bf16 inputs are widened exactly), ties to even: the hardware
+// convert rounds that way but turns magnitudes from 464 up into NaN, so the
+// quotient is clamped to +-448 first (saturation); NaN becomes code 0x7F.
+template <bool BF>
+__global__ __launch_bounds__(256) void kv_write_fp8_kernel(KvWriteFp8Args a) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = 2LL * a.row_chunks;  // K chunks then V chunks
+  if (item >= static_cast<int64_t>(a.num_tokens) * per_token) return;
+  const int t = static_cast<int>(item / per_token);
+  int c = static_cast<int>(item - static_cast<int64_t>(t) * per_token);
+  const bool is_v = c >= a.row_chunks;
+  if (is_v) c -= a.row_chunks;
+  const int slot = a.slot_mapping[t];
+  if (slot < 0 || static_cast<int64_t>(slot) >= a.num_slots) return;
+  const int h = c / a.head_chunks;
+  const int e = c - h * a.head_chunks;
+  const int blk = slot / a.block_size;
+  const int off = slot - blk * a.block_size;
+  const int64_t dst =
+      ((static_cast<int64_t>(blk) * a.num_kv_heads + h) * a.block_size + off) * a.head_chunks + e;
+  // 16 source elements: 2 (bf16) or 4 (f32) 16-byte chunks
+  constexpr int SRC_CHUNKS = BF ? 2 : 4;
+  const u32x4* in = static_cast<const u32x4*>(is_v ? a.v : a.k) +
+                    (static_cast<int64_t>(t) * a.row_chunks + c) * SRC_CHUNKS;
+  u32x4 w[SRC_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < SRC_CHUNKS; ++i) w[i] = __builtin_nontemporal_load(in + i);
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (BF) {
+      const uint32_t word = w[i / 8][(i % 8) / 2];
+      x[i] = (i & 1) ? bf16_hi(word) : bf16_lo(word);
+    } else {
+      x[i] = __uint_as_float(w[i / 4][i % 4]);
+    }
+  }
+  const float scale = is_v ? a.v_scale[0] : a.k_scale[0];
+  u32x4 out;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    float y[4];
+    uint32_t nan_mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q = x[4 * d + i] / scale;
+      nan_mask |= (q != q) ? (0xFFu << (8 * i)) : 0u;
+      y[i] = fminf(fmaxf(q, -448.f), 448.f);
+    }
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+    out[d] = (static_cast<uint32_t>(r) & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
+  }
+  u32x4* pool = is_v ? a.v_cache : a.k_cache;
+  pool[dst] = out;
+}
+
+hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(a.num_tokens) * 2 * a.row_chunks;
+  if (items == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  if (src == DType::BF16)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_write_fp8_kernel<false>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(a.num_tokens) * 2 * a.row_chunks;
   if (items == 0) return hipSuccess;

@@ -25,8 +25,10 @@ EXPORTED_SYMBOLS = (
     "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
-    "paged_prefill_window", "paged_attention_reduce_window",
+    "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
+    "paged_attention_decode_fp8",
 )
+FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -75,6 +77,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.varlen_causal_prefill_window.restype = i32
     lib.varlen_causal_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  f32, i32, i32, vp]
+    lib.paged_kv_write_fp8.restype = i32
+    lib.paged_kv_write_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+    lib.paged_attention_decode_fp8.restype = i32
+    lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                               f32, vp, vp, i32, i32, vp]
     lib.paged_attention_reduce_window.restype = i32
     lib.paged_attention_reduce_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.paged_prefill_window.restype = i32
@@ -122,13 +130,28 @@ def set_force_vector_path(on: bool) -> None:
     _check(lib.pa_set_option(PA_OPT_FORCE_VECTOR_PATH, int(bool(on))))
 
 
+def _scale_ptr(t: Optional[torch.Tensor], name: str) -> int:
+    if t is None:
+        raise ValueError(f"{name} is required for an FP8 (E4M3) pool")
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold one float32")
+    return _dev(t, name, torch.float32)
+
+
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
-                   v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
-    """Scatter k/v [T, H_kv, d] into the pools [NB, H_kv, bs, d] by slot (in place)."""
+                   v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None) -> None:
+    """Scatter k/v [T, H_kv, d] into the pools [NB, H_kv, bs, d] by slot (in place).
+    Pools of uint8 / float8_e4m3fn hold E4M3 codes: k_scale / v_scale (one-element
+    float32 device tensors) are then required and the rows are quantised."""
     lib = load_library()
     dt = _dtype_code(k)
+    fp8 = k_cache.dtype in FP8_POOL_DTYPES
     for name, t in (("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.dtype != k.dtype:
+        if fp8 and name != "v":
+            if t.dtype != k_cache.dtype:
+                raise TypeError(f"{name} dtype {t.dtype} != k_cache dtype {k_cache.dtype}")
+        elif t.dtype != k.dtype:
             raise TypeError(f"{name} dtype {t.dtype} != k dtype {k.dtype}")
     pk = _dev(k, "k", ndim=3)
     pv = _dev(v, "v", ndim=3)
@@ -141,6 +164,10 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("paged_kv_write: inconsistent shapes")
     if slot_mapping.shape[0] != T:
         raise ValueError("paged_kv_write: slot_mapping length != num_tokens")
+    if fp8:
+        _check(lib.paged_kv_write_fp8(pk, pv, pkc, pvc, ps, T, H, d, bs, NB, _scale_ptr(k_scale, "k_scale"),
+                                      _scale_ptr(v_scale, "v_scale"), dt, _stream(k)))
+        return
     _check(lib.paged_kv_write(pk, pv, pkc, pvc, ps, T, H, d, bs, NB, dt, _stream(k)))
 
 
@@ -154,15 +181,19 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            partition_size: int = 0, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            part_out: Optional[torch.Tensor] = None,
-                           part_lse: Optional[torch.Tensor] = None, window: int = 0
+                           part_lse: Optional[torch.Tensor] = None, window: int = 0,
+                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None
                            ) -> Tuple[torch.Tensor, torch.Tensor]:
     """PagedAttention decode.  Returns (out, lse), or (part_out, part_lse) when split.
-    window > 0 keeps only the last `window` positions (sliding window)."""
+    window > 0 keeps only the last `window` positions (sliding window).  Pools of
+    uint8 / float8_e4m3fn hold E4M3 codes read with k_scale / v_scale."""
     lib = load_library()
     dt = _dtype_code(q)
     B, Hq, d = q.shape
     NB, Hkv, bs, d2 = k_cache.shape
-    if d2 != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+    fp8 = k_cache.dtype in FP8_POOL_DTYPES
+    kv_dtype_ok = (v_cache.dtype == k_cache.dtype) and (fp8 or k_cache.dtype == q.dtype)
+    if d2 != d or v_cache.shape != k_cache.shape or not kv_dtype_ok:
         raise ValueError("paged_attention_decode: inconsistent q / cache shapes or dtypes")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("paged_attention_decode: block_tables / context_lens shape")
@@ -193,9 +224,16 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             raise ValueError("paged_attention_decode: out/lse shape")
         po = _dev(out, "out", q.dtype)
         pl = _dev(lse, "lse", torch.float32)
-    _check(lib.paged_attention_decode_window(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
-                                             block_tables.shape[1], NB, int(partition_size),
-                                             int(max_context_len), float(scale), int(window), dt, _stream(q)))
+    if fp8:
+        _check(lib.paged_attention_decode_fp8(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
+                                              block_tables.shape[1], NB, int(partition_size),
+                                              int(max_context_len), float(scale), _scale_ptr(k_scale, "k_scale"),
+                                              _scale_ptr(v_scale, "v_scale"), int(window), dt, _stream(q)))
+    else:
+        _check(lib.paged_attention_decode_window(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
+                                                 block_tables.shape[1], NB, int(partition_size),
+                                                 int(max_context_len), float(scale), int(window), dt,
+                                                 _stream(q)))
     if partition_size > 0:
         return part_out, part_lse
     return out, lse

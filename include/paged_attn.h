@@ -8,7 +8,8 @@
  *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
  * and a fifth extends prefill to a cached prefix:
  *   paged_prefill           a chunk of query rows against its sequence's paged cache
- * The four attention calls also come in *_window forms (sliding window).
+ * The four attention calls also come in *_window forms (sliding window), and the
+ * cache write and decode in *_fp8 forms over an FP8 (E4M3) cache.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -266,6 +267,48 @@ int paged_prefill_window(void* out, float* lse, const void* q, const void* k_cac
                          int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
                          int max_context_len, float scale, int window, pa_dtype dtype,
                          void* stream);
+
+/*
+ * FP8 KV cache.  "Llama 4 inference doubling (FlashAttention-3 + PagedAttention + vLLM)"
+ * turns on KV-cache quantisation (section 3.2) and pairs GQA with FP8 under dynamic
+ * scaling (chapter 1) without fixing the format; here the pools hold OCP FP8 E4M3
+ * codes (uint8: sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals,
+ * S.1111.111 = NaN, largest finite 448), one fp32 scale per pool, value = code * scale.
+ * Pools are [num_blocks, num_kv_heads, block_size, head_dim] bytes.
+ *
+ * paged_kv_write_fp8 - paged_kv_write into E4M3 pools.  For each token with a slot,
+ *   every element x of k (v) becomes the E4M3 code nearest to the IEEE fp32 quotient
+ *   x / *k_scale (x / *v_scale), ties to the even code; quotients of magnitude 448 or
+ *   more become +-448 (saturation); NaN becomes 0x7F.  bf16 inputs are widened
+ *   exactly first.  k_scale and v_scale point to one float each in DEVICE memory
+ *   (so a scale computed on the GPU needs no host round trip); a zero, negative or
+ *   non-finite scale gives unspecified codes.  k, v: [num_tokens, H_kv, head_dim],
+ *   dtype f32 or bf16.  Supported: head_dim a multiple of 16.  Other arguments and
+ *   errors as paged_kv_write.
+ *
+ * paged_attention_decode_fp8 - paged_attention_decode_window over E4M3 pools: the
+ *   attention of the dequantised K and V (code * scale), computed with bf16 matrix
+ *   products on the exact bf16 image of each code (every E4M3 value is a bf16 value),
+ *   the K scale folded into `scale` and the V scale into the output.  q, out, lse,
+ *   part_out, part_lse, window and the split-KV contract as in
+ *   paged_attention_decode_window; merge split results with
+ *   paged_attention_reduce_window.  Supported: dtype bf16 (queries and output),
+ *   head_dim 128, block_size 16, 32 or 64, H_q / H_kv in {1, 2, 4, 8}; anything else
+ *   is PA_ERR_UNSUPPORTED.
+ */
+int paged_kv_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                       const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                       int head_dim, int block_size, int num_blocks, const float* k_scale,
+                       const float* v_scale, pa_dtype dtype, void* stream);
+
+int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* part_lse,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               int partition_size, int max_context_len, float scale,
+                               const float* k_scale, const float* v_scale, int window,
+                               pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

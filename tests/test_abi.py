@@ -150,3 +150,23 @@ def test_window_validation(lib):
 def test_option(lib):
     assert lib.pa_set_option(99, 1) == 1
     assert lib.pa_set_option(ops.PA_OPT_FORCE_VECTOR_PATH, 0) == 0
+
+
+def test_fp8_validation(lib):
+    p = ctypes.c_void_p(16)
+    # write: null scale pointers, head_dim not a multiple of 16, nothing to do
+    assert lib.paged_kv_write_fp8(p, p, p, p, p, 4, 8, 128, 16, 10, None, p, 1, None) == 1
+    assert lib.paged_kv_write_fp8(p, p, p, p, p, 4, 8, 72, 16, 10, p, p, 1, None) == 2
+    assert lib.paged_kv_write_fp8(p, p, p, p, p, 0, 8, 128, 16, 10, p, p, 1, None) == 0
+    # decode: f32 queries, head_dim 64, block_size 8, group 16 are unsupported;
+    # a negative window or null scales are invalid
+    args = lambda **kw: [p, p, p, p, p, p, p, p, p, kw.get("B", 2), kw.get("Hq", 32), kw.get("Hkv", 8),
+                         kw.get("d", 128), kw.get("bs", 16), kw.get("mbps", 8), 20, 0, 128, 0.1, kw.get("ks", p), p,
+                         kw.get("w", 0), kw.get("dt", 1), None]
+    assert lib.paged_attention_decode_fp8(*args(dt=0)) == 2
+    assert lib.paged_attention_decode_fp8(*args(d=64)) == 2
+    assert lib.paged_attention_decode_fp8(*args(bs=8, mbps=16)) == 2
+    assert lib.paged_attention_decode_fp8(*args(Hq=32, Hkv=2)) == 2
+    assert lib.paged_attention_decode_fp8(*args(w=-1)) == 1
+    assert lib.paged_attention_decode_fp8(*args(ks=None)) == 1
+    assert lib.paged_attention_decode_fp8(*args(B=0)) == 0
