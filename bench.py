@@ -82,6 +82,7 @@ def main(argv=None):
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window figures")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -418,6 +419,75 @@ def main(argv=None):
         del wcopies
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------- FP8 cache
+    fp8 = None
+    if not args.no_fp8:
+        t0 = time.perf_counter()
+        fc = wl.make_case(8)
+        fB, fHq, fHkv, fd = fc.spec.batch, fc.spec.num_q_heads, fc.spec.num_kv_heads, fc.spec.head_dim
+        log(f"fp8 workload generated in {time.perf_counter() - t0:.1f}s: NB={fc.num_blocks}")
+        fbytes = int(fc.context_lens.astype(np.int64).sum()) * fHkv * 2 * fd   # one byte per element
+        fP = ops.num_partitions(fc.max_context_len, ps)
+        # the newest token of each sequence (its last row of the written history)
+        last = np.cumsum(fc.context_lens.astype(np.int64)) - 1
+        ks_d = torch.tensor([fc.k_scale], dtype=torch.float32, device=dev)
+        vs_d = torch.tensor([fc.v_scale], dtype=torch.float32, device=dev)
+        fk_all, fv_all, fslots = up(fc.k_new), up(fc.v_new), up(fc.slot_mapping)
+        fcopies = []
+        for _ in range(max(1, args.copies)):
+            c = dict(q=up(fc.q), kc=up(fc.k_cache), vc=up(fc.v_cache), bt=up(fc.block_tables),
+                     cl=up(fc.context_lens), kn=up(fc.k_new[last]), vn=up(fc.v_new[last]),
+                     slots=up(fc.slot_mapping[last]),
+                     po=torch.empty((fB, fHq, fP, fd), dtype=torch.float32, device=dev),
+                     pl=torch.empty((fB, fHq, fP), dtype=torch.float32, device=dev),
+                     out=torch.empty((fB, fHq, fd), dtype=torch.bfloat16, device=dev),
+                     lse=torch.empty((fB, fHq), dtype=torch.float32, device=dev))
+            ops.paged_kv_write(fk_all, fv_all, c["kc"], c["vc"], fslots, k_scale=ks_d, v_scale=vs_d)
+            fcopies.append(c)
+        del fk_all, fv_all
+
+        def fdecode(c):
+            ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], fc.max_context_len, fc.scale,
+                                       ps, part_out=c["po"], part_lse=c["pl"], k_scale=ks_d, v_scale=vs_d)
+
+        def fstep(c):
+            ops.paged_kv_write(c["kn"], c["vn"], c["kc"], c["vc"], c["slots"], k_scale=ks_d, v_scale=vs_d)
+            fdecode(c)
+            ops.paged_attention_reduce(c["po"], c["pl"], c["cl"], ps, out=c["out"], lse=c["lse"])
+
+        def ftimed(fn, n_groups):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n_groups)]
+            torch.cuda.synchronize()
+            for gi in range(n_groups):
+                evs[gi][0].record(stream)
+                for k in range(group):
+                    fn(fcopies[(gi * group + k) % len(fcopies)])
+                evs[gi][1].record(stream)
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) / group for a, b in evs]
+        for i in range(args.warmup):
+            fstep(fcopies[i % len(fcopies)])
+        fg = max(1, args.steps // group)
+        fdec_ms = ftimed(fdecode, fg)
+        fstep_ms = ftimed(fstep, fg)
+        favg = float(np.mean(fdec_ms))
+        fgbs = fbytes / (favg * 1e-3) / 1e9
+        fsms = float(np.mean(fstep_ms))
+        fp8 = {"workload": fc.spec.name, "partition_size": ps, "k_scale": fc.k_scale, "v_scale": fc.v_scale,
+               "sum_context": int(fc.context_lens.sum()), "kv_bytes_per_step": fbytes,
+               "step_us": round(fsms * 1e3, 2), "step_gbs": round(fbytes / (fsms * 1e-3) / 1e9, 1),
+               "decode_tokens_per_s": round(fB / (fsms * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(fgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "decode_mfma_kernel<G=4,BS=16,W=1,KV8> (paged_attention_decode_fp8)",
+                            "kernel_avg_us": round(favg * 1e3, 2),
+                            "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
+                            "algorithmic_bytes_per_launch": fbytes}}
+        log(f"fp8 decode kernel {favg * 1e3:.1f} us -> {fgbs:.0f} GB/s of E4M3 KV; step {fsms * 1e3:.1f} us")
+        del fcopies
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -472,6 +542,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "prefill": prefill,
         "window": window,
+        "fp8": fp8,
     }
     print(json.dumps(line), flush=True)
 
