@@ -45,6 +45,9 @@ PREFILL_SOURCES = ("attention_paged_kv_write_amd/csrc/prefill.hip",
                    "attention_paged_kv_write_amd/csrc/kernels.h")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama3_8b.txt")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_llama3_8b.txt")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_fp8_llama3_8b.txt")
+PAGED_PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_prefill_llama3_8b.txt")
+WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_window_llama3_8b.txt")
 
 
 def log(msg):
@@ -232,7 +235,6 @@ def main(argv=None):
 
     # ----------------------------------------------------------------- prefill
     prefill = None
-    window_prefill = None
     if not args.no_prefill:
         t0 = time.perf_counter()
         pc = wl.make_case(3)
@@ -314,42 +316,13 @@ def main(argv=None):
                          "kernel_avg_us": round(cms * 1e3, 1), "tflops": round(ctf, 1),
                          "roofline": {"bound": "mfma", "achieved": round(ctf, 1), "peak": BF16_PEAK_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(ctf / BF16_PEAK_TFLOPS, 4),
-                                      "traffic": None,
+                                      "traffic": measured_traffic(PAGED_PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
                                       "kernel": "prefill_mfma_kernel<NW=4, paged> (paged_prefill)",
                                       "algorithmic_flops_per_launch": cflops},
                          "tokens_per_s": round(cc.total_q / (cms * 1e-3), 1)}
         prefill["paged_prefill"] = paged_prefill
         log(f"paged prefill {cms * 1e3:.1f} us -> {ctf:.1f} TFLOP/s")
 
-        # the same chunks under a sliding window of 2048 keys: row at position p
-        # sees min(p + 1, 2048) keys
-        if not args.no_window:
-            PW = 2048
-            vis = np.concatenate([np.minimum(np.arange(p0, p0 + n) + 1, PW) for p0, n in zip(pre, lq)])
-            wflops = 4.0 * cc.spec.head_dim * cc.spec.num_q_heads * float(vis.sum())
-
-            def chunked_w():
-                ops.paged_prefill(cq, ckc, cvc, cbt, ccu, ccl, cc.max_seqlen_q, cc.max_context_len, cc.scale,
-                                  out=cout, lse=clse, window=PW)
-            for _ in range(3):
-                chunked_w()
-            torch.cuda.synchronize()
-            pa_.record(stream)
-            for _ in range(args.prefill_iters):
-                chunked_w()
-            pb_.record(stream)
-            torch.cuda.synchronize()
-            wpms = pa_.elapsed_time(pb_) / args.prefill_iters
-            wtf = wflops / (wpms * 1e-3) / 1e12
-            window_prefill = {"workload": cc.spec.name, "window": PW, "kernel_avg_us": round(wpms * 1e3, 1),
-                              "tflops": round(wtf, 1),
-                              "roofline": {"bound": "mfma", "achieved": round(wtf, 1), "peak": BF16_PEAK_TFLOPS,
-                                           "unit": "TFLOP/s", "frac": round(wtf / BF16_PEAK_TFLOPS, 4),
-                                           "traffic": None,
-                                           "kernel": "prefill_mfma_kernel<NW=4, paged> (paged_prefill_window)",
-                                           "algorithmic_flops_per_launch": wflops},
-                              "flops_vs_no_window": round(wflops / cflops, 4)}
-            log(f"windowed paged prefill {wpms * 1e3:.1f} us -> {wtf:.1f} TFLOP/s")
         del ckc, cvc, cq, cout
         torch.cuda.empty_cache()
 
@@ -408,16 +381,61 @@ def main(argv=None):
                   "step_us": round(float(np.mean(wstep_ms)) * 1e3, 2),
                   "step_gbs": round(wbytes / (float(np.mean(wstep_ms)) * 1e-3) / 1e9, 1),
                   "roofline": {"bound": "hbm", "achieved": round(wgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": round(wgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                               "frac": round(wgbs / HBM_PEAK_GBS, 4),
+                               "traffic": measured_traffic(WINDOW_TRAFFIC_FILE, DECODE_SOURCES),
                                "kernel": "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode_window)",
                                "kernel_avg_us": round(wavg * 1e3, 2),
                                "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
                                "algorithmic_bytes_per_launch": wbytes},
                   "decode_tokens_per_s": round(wB / (float(np.mean(wstep_ms)) * 1e-3), 1),
-                  "paged_prefill": window_prefill}
+                  "paged_prefill": None}
         log(f"window decode kernel {wavg * 1e3:.1f} us -> {wgbs:.0f} GB/s; step {np.mean(wstep_ms) * 1e3:.1f} us")
         del wcopies
         torch.cuda.empty_cache()
+
+        # chunked prefill (workload 6) under the same 2048-key window: the row at
+        # position p sees min(p + 1, 2048) keys (runs with the window figures,
+        # whatever --no-prefill says)
+        if True:
+            cc = wl.make_case(6)
+            lq = np.diff(cc.cu_seqlens_q).astype(np.int64)
+            pre = cc.context_lens.astype(np.int64) - lq
+            cflops = 4.0 * cc.spec.head_dim * cc.spec.num_q_heads * float((lq * pre + lq * (lq + 1) // 2).sum())
+            PW = W
+            vis = np.concatenate([np.minimum(np.arange(p0, p0 + n) + 1, PW) for p0, n in zip(pre, lq)])
+            wflops = 4.0 * cc.spec.head_dim * cc.spec.num_q_heads * float(vis.sum())
+            ckc, cvc = up(cc.k_cache), up(cc.v_cache)
+            ops.paged_kv_write(up(cc.k_new), up(cc.v_new), ckc, cvc, up(cc.slot_mapping))
+            cq, cbt, ccu, ccl = up(cc.q), up(cc.block_tables), up(cc.cu_seqlens_q), up(cc.context_lens)
+            cout = torch.empty_like(cq)
+            clse = torch.empty((cc.total_q, cc.spec.num_q_heads), dtype=torch.float32, device=dev)
+
+            def chunked_w():
+                ops.paged_prefill(cq, ckc, cvc, cbt, ccu, ccl, cc.max_seqlen_q, cc.max_context_len, cc.scale,
+                                  out=cout, lse=clse, window=PW)
+            for _ in range(3):
+                chunked_w()
+            torch.cuda.synchronize()
+            pa_, pb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            pa_.record(stream)
+            for _ in range(args.prefill_iters):
+                chunked_w()
+            pb_.record(stream)
+            torch.cuda.synchronize()
+            wpms = pa_.elapsed_time(pb_) / args.prefill_iters
+            wtf = wflops / (wpms * 1e-3) / 1e12
+            window_prefill = {"workload": cc.spec.name, "window": PW, "kernel_avg_us": round(wpms * 1e3, 1),
+                              "tflops": round(wtf, 1),
+                              "roofline": {"bound": "mfma", "achieved": round(wtf, 1), "peak": BF16_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(wtf / BF16_PEAK_TFLOPS, 4),
+                                           "traffic": None,
+                                           "kernel": "prefill_mfma_kernel<NW=4, paged> (paged_prefill_window)",
+                                           "algorithmic_flops_per_launch": wflops},
+                              "flops_vs_no_window": round(wflops / cflops, 4)}
+            log(f"windowed paged prefill {wpms * 1e3:.1f} us -> {wtf:.1f} TFLOP/s")
+            window["paged_prefill"] = window_prefill
+            del ckc, cvc, cq, cout
+            torch.cuda.empty_cache()
 
     # ------------------------------------------------------------- FP8 cache
     fp8 = None
@@ -479,7 +497,8 @@ def main(argv=None):
                "step_us": round(fsms * 1e3, 2), "step_gbs": round(fbytes / (fsms * 1e-3) / 1e9, 1),
                "decode_tokens_per_s": round(fB / (fsms * 1e-3), 1),
                "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(fgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "frac": round(fgbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(FP8_TRAFFIC_FILE, DECODE_SOURCES),
                             "kernel": "decode_mfma_kernel<G=4,BS=16,W=1,KV8> (paged_attention_decode_fp8)",
                             "kernel_avg_us": round(favg * 1e3, 2),
                             "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
