@@ -10,3 +10,4 @@ from .attention import (  # noqa: F401
 )
 from .e4m3 import E4M3, E4M3_MAX, E4M3_NAN, e4m3_encode, e4m3_value  # noqa: F401
 from .fp8 import dequantize, kv_write_fp8, quantize  # noqa: F401
+from . import rope  # noqa: F401
