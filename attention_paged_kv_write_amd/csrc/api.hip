@@ -185,6 +185,61 @@ int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* pa
   return launch_status(pa::launch_decode_fp8(a, head_dim, static_cast<hipStream_t>(stream)), fn);
 }
 
+int rope_cos_sin_cache(float* cos_sin, int max_positions, int rot_dim, double base, void* stream) {
+  const char* fn = "rope_cos_sin_cache";
+  if (max_positions < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_positions < 0", fn);
+  if (rot_dim <= 0 || rot_dim % 2 != 0) return fail(PA_ERR_INVALID_ARG, "%s: rot_dim must be even and positive", fn);
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(PA_ERR_INVALID_ARG, "%s: base must be finite and > 1", fn);
+  if (static_cast<int64_t>(max_positions) * rot_dim > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "%s: table too large", fn);
+  if (max_positions == 0) return ok();
+  if (!cos_sin) return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return launch_status(pa::launch_rope_cos_sin(cos_sin, max_positions, rot_dim, base,
+                                               static_cast<hipStream_t>(stream)), fn);
+}
+
+int paged_kv_write_rope(void* q, void* k, const void* v, void* k_cache, void* v_cache,
+                        const int32_t* slot_mapping, const int32_t* positions, const float* cos_sin,
+                        int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
+                        int block_size, int num_blocks, int max_positions, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_kv_write_rope";
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", fn);
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_positions <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (rot_dim <= 0 || rot_dim % 2 != 0 || rot_dim > head_dim)
+    return fail(PA_ERR_INVALID_ARG, "%s: rot_dim must be even, positive and <= head_dim", fn);
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_blocks * block_size exceeds int32 slots", fn);
+  const int es = esize(dtype);
+  if ((static_cast<int64_t>(head_dim) * es) % 16 != 0 || (static_cast<int64_t>(rot_dim / 2) * es) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim and rot_dim/2 must fill whole 16-byte chunks", fn);
+  if (num_tokens == 0) return ok();
+  if (!q || !k || !v || !k_cache || !v_cache || !slot_mapping || !positions || !cos_sin)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::RopeWriteArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_cache = static_cast<pa::u32x4*>(k_cache);
+  a.v_cache = static_cast<pa::u32x4*>(v_cache);
+  a.slot_mapping = slot_mapping;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_chunks = head_dim * es / 16;
+  a.pair_chunks = rot_dim / 2 * es / 16;
+  a.rot_dim = rot_dim;
+  a.block_size = block_size;
+  a.max_positions = max_positions;
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+  return launch_status(pa::launch_rope_kv_write(a, dt, static_cast<hipStream_t>(stream)), fn);
+}
+
 int paged_attention_decode(void* out, float* lse, float* part_out, float* part_lse, const void* q,
                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
                            const int32_t* context_lens, int num_seqs, int num_q_heads,

@@ -38,6 +38,27 @@ struct KvWriteFp8Args {
   int64_t num_slots;
 };
 
+// RoPE fused into the cache write (rope.hip).
+struct RopeWriteArgs {
+  void* q;                     // [T, H_q, d], rotated in place
+  void* k;                     // [T, H_kv, d], rotated in place
+  const void* v;               // [T, H_kv, d]
+  u32x4* k_cache;              // [NB, H_kv, bs, d] as 16-byte chunks
+  u32x4* v_cache;
+  const int32_t* slot_mapping; // [T]
+  const int32_t* positions;    // [T]
+  const float* cos_sin;        // [max_positions, rot_dim]: cos then sin
+  int num_tokens;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_chunks;             // d * sizeof(T) / 16
+  int pair_chunks;             // rot_dim / 2 * sizeof(T) / 16
+  int rot_dim;
+  int block_size;
+  int max_positions;
+  int64_t num_slots;
+};
+
 struct DecodeArgs {
   void* out;             // [B, H_q, d] (T)        when partition_size == 0
   float* lse;            // [B, H_q]               when partition_size == 0
@@ -106,6 +127,8 @@ enum class DType { F32 = 0, BF16 = 1 };
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_rope_cos_sin(float* table, int max_positions, int rot_dim, double base, hipStream_t stream);
+hipError_t launch_rope_kv_write(const RopeWriteArgs& a, DType dt, hipStream_t stream);
 
 // Returns hipErrorNotSupported when no kernel instance covers the shape.
 hipError_t launch_decode(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);

@@ -26,7 +26,7 @@ EXPORTED_SYMBOLS = (
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
-    "paged_attention_decode_fp8",
+    "paged_attention_decode_fp8", "rope_cos_sin_cache", "paged_kv_write_rope",
 )
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
 
@@ -83,6 +83,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                f32, vp, vp, i32, i32, vp]
+    lib.rope_cos_sin_cache.restype = i32
+    lib.rope_cos_sin_cache.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+    lib.paged_kv_write_rope.restype = i32
+    lib.paged_kv_write_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, vp]
     lib.paged_attention_reduce_window.restype = i32
     lib.paged_attention_reduce_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.paged_prefill_window.restype = i32
@@ -169,6 +174,44 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
                                       _scale_ptr(v_scale, "v_scale"), dt, _stream(k)))
         return
     _check(lib.paged_kv_write(pk, pv, pkc, pvc, ps, T, H, d, bs, NB, dt, _stream(k)))
+
+
+def rope_cos_sin_cache(max_positions: int, rot_dim: int, base: float = 10000.0,
+                       device: Optional[torch.device] = None) -> torch.Tensor:
+    """The RoPE table [max_positions, rot_dim] float32 (cos then sin per row)."""
+    lib = load_library()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    table = torch.empty((max_positions, rot_dim), dtype=torch.float32, device=dev)
+    _check(lib.rope_cos_sin_cache(table.data_ptr() if table.numel() else None, int(max_positions), int(rot_dim),
+                                  float(base), torch.cuda.current_stream(dev).cuda_stream))
+    return table
+
+
+def paged_kv_write_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, slot_mapping: torch.Tensor, positions: torch.Tensor,
+                        cos_sin: torch.Tensor) -> None:
+    """Rotate q [T,H_q,d] and k [T,H_kv,d] in place at `positions` with the table
+    `cos_sin` [max_positions, rot_dim], and write rotated k and v into the pools."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    T, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if k.shape != (T, Hkv, d) or v.shape != k.shape or v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("paged_kv_write_rope: inconsistent shapes")
+    if slot_mapping.shape != (T,) or positions.shape != (T,):
+        raise ValueError("paged_kv_write_rope: slot_mapping / positions length != num_tokens")
+    if cos_sin.dim() != 2:
+        raise ValueError("paged_kv_write_rope: cos_sin must be [max_positions, rot_dim]")
+    P, rot = cos_sin.shape
+    _check(lib.paged_kv_write_rope(_dev(q, "q", ndim=3), _dev(k, "k", ndim=3), _dev(v, "v", ndim=3),
+                                   _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                                   _dev(slot_mapping, "slot_mapping", torch.int32, 1),
+                                   _dev(positions, "positions", torch.int32, 1),
+                                   _dev(cos_sin, "cos_sin", torch.float32, 2),
+                                   T, Hq, Hkv, d, rot, bs, NB, P, dt, _stream(q)))
 
 
 def num_partitions(max_context_len: int, partition_size: int) -> int:

@@ -8,8 +8,9 @@
  *   varlen_causal_prefill   causal attention of sequences packed by cu_seqlens
  * and a fifth extends prefill to a cached prefix:
  *   paged_prefill           a chunk of query rows against its sequence's paged cache
- * The four attention calls also come in *_window forms (sliding window), and the
- * cache write and decode in *_fp8 forms over an FP8 (E4M3) cache.
+ * The four attention calls also come in *_window forms (sliding window), the cache
+ * write and decode in *_fp8 forms over an FP8 (E4M3) cache, and the cache write in a
+ * *_rope form that applies rotary position embedding to q and k in the same pass.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -309,6 +310,37 @@ int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* pa
                                int partition_size, int max_context_len, float scale,
                                const float* k_scale, const float* v_scale, int window,
                                pa_dtype dtype, void* stream);
+
+/*
+ * Rotary position embedding fused into the cache write.  "LLaMA inference performance:
+ * structure and source" (section 2.2, and step 1 of its attention listing) turns each
+ * query and key vector by a position-dependent rotation computed from sin and cos, with
+ * the table of those values worth precomputing; the pairing and frequencies are not
+ * printed.  Here dims i and i + rot_dim/2 (i < rot_dim/2) of the first rot_dim dims of a
+ * head form a pair, turned at position p by the angle p * base^(-2i/rot_dim):
+ *   y_i = x_i cos - x_{i+rot_dim/2} sin,   y_{i+rot_dim/2} = x_{i+rot_dim/2} cos + x_i sin.
+ *
+ * rope_cos_sin_cache - fill the table cos_sin [max_positions, rot_dim] (float32, device):
+ *   row p holds cos(p theta_i) for i < rot_dim/2, then sin(p theta_i); angles, cos and sin
+ *   are evaluated in double precision and rounded once to float.  rot_dim even and
+ *   positive; base finite and > 1 (10000 for LLaMA).
+ *
+ * paged_kv_write_rope - one pass over a step's rows: q [num_tokens, H_q, head_dim] and
+ *   k [num_tokens, H_kv, head_dim] are rotated IN PLACE (token t at position positions[t],
+ *   int32, read from cos_sin row positions[t]; arithmetic in float32, results rounded to
+ *   dtype, nearest even), and the rotated k and the unrotated v are written into the
+ *   pools exactly as paged_kv_write does (slot_mapping; s < 0 rotates q and k but writes
+ *   nothing).  Dims past rot_dim pass through.  Positions outside [0, max_positions) give
+ *   unspecified values (no access outside the table).  q, k, v must not overlap.
+ *   Supported: dtype f32 or bf16 with head_dim * sizeof(dtype) and rot_dim/2 * sizeof(dtype)
+ *   multiples of 16 bytes; rot_dim <= head_dim.
+ */
+int rope_cos_sin_cache(float* cos_sin, int max_positions, int rot_dim, double base, void* stream);
+
+int paged_kv_write_rope(void* q, void* k, const void* v, void* k_cache, void* v_cache,
+                        const int32_t* slot_mapping, const int32_t* positions, const float* cos_sin,
+                        int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
+                        int block_size, int num_blocks, int max_positions, pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -170,3 +170,17 @@ def test_fp8_validation(lib):
     assert lib.paged_attention_decode_fp8(*args(w=-1)) == 1
     assert lib.paged_attention_decode_fp8(*args(ks=None)) == 1
     assert lib.paged_attention_decode_fp8(*args(B=0)) == 0
+
+
+def test_rope_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.rope_cos_sin_cache(p, 16, 7, 10000.0, None) == 1        # odd rot_dim
+    assert lib.rope_cos_sin_cache(p, 16, 64, 1.0, None) == 1           # base must exceed 1
+    assert lib.rope_cos_sin_cache(None, 0, 64, 10000.0, None) == 0     # empty table
+    call = lambda **kw: lib.paged_kv_write_rope(p, p, p, p, p, p, p, p, kw.get("T", 4), 32, 8, kw.get("d", 128),
+                                                kw.get("rot", 128), 16, 10, kw.get("P", 4096), kw.get("dt", 1), None)
+    assert call(rot=130) == 1            # rot_dim > head_dim
+    assert call(rot=24) == 2             # rot_dim/2 not a whole number of 16-byte bf16 chunks
+    assert call(P=0) == 1
+    assert call(T=0) == 0
+    assert call(dt=0, rot=20) == 2       # f32: 10 floats = 40 bytes, not whole chunks

@@ -19,6 +19,7 @@ HOT = {
     "decode.hip": ("decode_mfma_kernel", "decode_generic_kernel"),
     "reduce.hip": ("reduce_kernel", "reduce_small_kernel"),
     "kv_write.hip": ("",),
+    "rope.hip": ("rope_kv_write_kernel",),
 }
 
 
