@@ -271,6 +271,35 @@ def main(argv=None):
         torch.cuda.synchronize()
         wms = float(np.mean([a.elapsed_time(b) for a, b in wev]))
         wbytes = 2 * 2 * pc.total_tokens * pc.spec.num_kv_heads * pc.spec.head_dim * 2  # read + write, K and V
+        # RoPE fused into the prompt's cache write (row positions 0 .. L-1 of each
+        # sequence, base 10000): q and k rotated in place, rotated k and v into
+        # the pool; on copies, since every call turns q and k again
+        cu_h = pc.cu_seqlens.astype(np.int64)
+        rpos = torch.from_numpy(np.concatenate([np.arange(cu_h[i + 1] - cu_h[i]) for i in range(len(cu_h) - 1)])
+                                .astype(np.int32)).to(dev)
+        rtab = ops.rope_cos_sin_cache(pc.max_seqlen, d_, 10000.0)
+        rq, rk = pq.clone(), pk.clone()
+        rope_bytes = (2 * T_ * Hq_ * d_ * 2 + 3 * T_ * Hkv_ * d_ * 2 + 2 * T_ * Hkv_ * d_ * 2
+                      + T_ * d_ * 4 + T_ * 8)
+        for _ in range(3):
+            ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
+        torch.cuda.synchronize()
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in rev:
+            a.record(stream)
+            ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
+            b.record(stream)
+        torch.cuda.synchronize()
+        rms = float(np.mean([a.elapsed_time(b) for a, b in rev]))
+        rgbs = rope_bytes / (rms * 1e-3) / 1e9
+        rope_write = {"workload": pc.spec.name + " prompt rows", "rot_dim": d_, "base": 10000.0,
+                      "kernel_avg_us": round(rms * 1e3, 1),
+                      "roofline": {"bound": "hbm", "achieved": round(rgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(rgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "kernel": "rope_kv_write_kernel<bf16> (paged_kv_write_rope)",
+                                   "algorithmic_bytes_per_launch": rope_bytes}}
+        log(f"fused rope + kv write {rms * 1e3:.1f} us -> {rgbs:.0f} GB/s")
+        del rq, rk
         prefill = {"workload": pc.spec.name, "total_tokens": pc.total_tokens,
                    "kernel_avg_us": round(pms * 1e3, 1), "tflops": round(tflops, 1),
                    "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
@@ -281,7 +310,8 @@ def main(argv=None):
                                 "algorithmic_bytes_per_launch": io_bytes},
                    "tokens_per_s": round(pc.total_tokens / (pms * 1e-3), 1),
                    "kv_write": {"kernel_avg_us": round(wms * 1e3, 1),
-                                "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)}}
+                                "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)},
+                   "rope_kv_write": rope_write}
         log(f"prefill {pms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; prompt kv write {wms * 1e3:.1f} us")
         del pq, pk, pv, pout, pool, pool_v
         torch.cuda.empty_cache()
