@@ -48,6 +48,10 @@ PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_llama3_8b
 FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_fp8_llama3_8b.txt")
 PAGED_PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_prefill_llama3_8b.txt")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_window_llama3_8b.txt")
+ROPE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_kv_write_llama3_8b.txt")
+ROPE_SOURCES = ("attention_paged_kv_write_amd/csrc/rope.hip",
+                "attention_paged_kv_write_amd/csrc/common.h",
+                "attention_paged_kv_write_amd/csrc/kernels.h")
 
 
 def log(msg):
@@ -295,7 +299,8 @@ def main(argv=None):
         rope_write = {"workload": pc.spec.name + " prompt rows", "rot_dim": d_, "base": 10000.0,
                       "kernel_avg_us": round(rms * 1e3, 1),
                       "roofline": {"bound": "hbm", "achieved": round(rgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(rgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "frac": round(rgbs / HBM_PEAK_GBS, 4),
+                                   "traffic": measured_traffic(ROPE_TRAFFIC_FILE, ROPE_SOURCES),
                                    "kernel": "rope_kv_write_kernel<bf16> (paged_kv_write_rope)",
                                    "algorithmic_bytes_per_launch": rope_bytes}}
         log(f"fused rope + kv write {rms * 1e3:.1f} us -> {rgbs:.0f} GB/s")
