@@ -41,6 +41,91 @@ int esize(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
+// Validation, arguments and launch shared by the decode entry points: plain or
+// sliding window, bf16/f32 or E4M3 pools (kv8, with device-side scales), and
+// with or without the new token's K/V (k_new, v_new) appended by the kernel.
+int decode_call(const char* fn, void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                int partition_size, int max_context_len, float scale, int window, pa_dtype dtype, bool kv8,
+                const float* k_scale, const float* v_scale, void* stream) {
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be 0 or a multiple of block_size", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
+  const int G = num_q_heads / num_kv_heads;
+  if (kv8) {
+    if (dtype != PA_BF16 || head_dim != 128)
+      return fail(PA_ERR_UNSUPPORTED, "%s: bf16 queries with head_dim 128 only", fn);
+    if (!(block_size == 16 || block_size == 32 || block_size == 64))
+      return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  } else {
+    if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+    if (!(block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64))
+      return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  }
+  if (!group_ok(G)) return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, G);
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
+  if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARG, "%s: null k_scale/v_scale", fn);
+  int num_parts = 1;
+  if (partition_size > 0) {
+    if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
+    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
+  } else if (!out || !lse) {
+    return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
+  }
+  pa::DecodeArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.num_partitions = num_parts;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * pa::kLog2e;
+  a.flat_units = 0;
+  a.window = window;
+  a.k_scale = kv8 ? k_scale : nullptr;
+  a.v_scale = kv8 ? v_scale : nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (kv8) {
+    e = pa::launch_decode_fp8(a, head_dim, s);
+  } else {
+    const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
+    e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s) : pa::launch_decode(a, dt, head_dim, s);
+  }
+  return launch_status(e, fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,72 +204,6 @@ int paged_kv_write_fp8(const void* k, const void* v, void* k_cache, void* v_cach
   return launch_status(pa::launch_kv_write_fp8(a, dt, static_cast<hipStream_t>(stream)), fn);
 }
 
-int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* part_lse, const void* q,
-                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                               const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
-                               int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
-                               int partition_size, int max_context_len, float scale, const float* k_scale,
-                               const float* v_scale, int window, pa_dtype dtype, void* stream) {
-  const char* fn = "paged_attention_decode_fp8";
-  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
-  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
-  if (num_q_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
-  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
-    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
-    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be 0 or a multiple of block_size", fn);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
-  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
-  if (dtype != PA_BF16 || head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "%s: bf16 queries with head_dim 128 only", fn);
-  if (!(block_size == 16 || block_size == 32 || block_size == 64))
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
-  const int G = num_q_heads / num_kv_heads;
-  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, G);
-  if (num_seqs == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !k_scale || !v_scale)
-    return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
-  int num_parts = 1;
-  if (partition_size > 0) {
-    if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
-    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
-    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
-  } else if (!out || !lse) {
-    return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
-  }
-  pa::DecodeArgs a;
-  a.out = out;
-  a.lse = lse;
-  a.part_out = part_out;
-  a.part_lse = part_lse;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.block_size = block_size;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.partition_size = partition_size;
-  a.num_partitions = num_parts;
-  a.max_context_len = max_context_len;
-  a.scale_log2 = scale * pa::kLog2e;
-  a.flat_units = 0;
-  a.window = window;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  return launch_status(pa::launch_decode_fp8(a, head_dim, static_cast<hipStream_t>(stream)), fn);
-}
-
 int rope_cos_sin_cache(float* cos_sin, int max_positions, int rot_dim, double base, void* stream) {
   const char* fn = "rope_cos_sin_cache";
   if (max_positions < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_positions < 0", fn);
@@ -258,67 +277,51 @@ int paged_attention_decode_window(void* out, float* lse, float* part_out, float*
                                   int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                                   int num_blocks, int partition_size, int max_context_len, float scale,
                                   int window, pa_dtype dtype, void* stream) {
-  const char* fn = "paged_attention_decode";
-  if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
-  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
-  if (num_q_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %% num_kv_heads != 0", fn);
-  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
-    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
-    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be 0 or a multiple of block_size", fn);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
-  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
-  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
-  if (!(block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64))
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
-  if (!group_ok(num_q_heads / num_kv_heads))
-    return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, num_q_heads / num_kv_heads);
-  if (num_seqs == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
-  int num_parts = 1;
-  if (partition_size > 0) {
-    if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
-    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
-    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
-  } else if (!out || !lse) {
-    return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
-  }
-  pa::DecodeArgs a;
-  a.out = out;
-  a.lse = lse;
-  a.part_out = part_out;
-  a.part_lse = part_lse;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.block_size = block_size;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.partition_size = partition_size;
-  a.num_partitions = num_parts;
-  a.max_context_len = max_context_len;
-  a.scale_log2 = scale * pa::kLog2e;
-  a.flat_units = 0;
-  a.window = window;
-  a.k_scale = nullptr;
-  a.v_scale = nullptr;
-  const pa::DType dt = dtype == PA_BF16 ? pa::DType::BF16 : pa::DType::F32;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = g_force_vector_path ? pa::launch_decode_generic(a, dt, head_dim, s)
-                                           : pa::launch_decode(a, dt, head_dim, s);
-  return launch_status(e, fn);
+  return decode_call("paged_attention_decode", out, lse, part_out, part_lse, q, nullptr, nullptr, k_cache,
+                     v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, partition_size, max_context_len, scale, window,
+                     dtype, false, nullptr, nullptr, stream);
+}
+
+int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                               int partition_size, int max_context_len, float scale, const float* k_scale,
+                               const float* v_scale, int window, pa_dtype dtype, void* stream) {
+  return decode_call("paged_attention_decode_fp8", out, lse, part_out, part_lse, q, nullptr, nullptr, k_cache,
+                     v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, partition_size, max_context_len, scale, window,
+                     dtype, true, k_scale, v_scale, stream);
+}
+
+int paged_attention_decode_append(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                                  const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int partition_size, int max_context_len,
+                                  float scale, int window, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode_append";
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "%s: null k_new/v_new", fn);
+  return decode_call(fn, out, lse, part_out, part_lse, q, k_new, v_new, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, partition_size, max_context_len, scale, window, dtype, false, nullptr, nullptr,
+                     stream);
+}
+
+int paged_attention_decode_append_fp8(void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                                      const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, int partition_size,
+                                      int max_context_len, float scale, const float* k_scale, const float* v_scale,
+                                      int window, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode_append_fp8";
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "%s: null k_new/v_new", fn);
+  return decode_call(fn, out, lse, part_out, part_lse, q, k_new, v_new, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, partition_size, max_context_len, scale, window, dtype, true, k_scale, v_scale,
+                     stream);
 }
 
 int paged_attention_reduce(void* out, float* lse, const float* part_out, const float* part_lse,

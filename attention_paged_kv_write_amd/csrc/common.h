@@ -146,4 +146,30 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>((uintptr_t)((lds_cptr)p));
 }
 
+// ---------------------------------------------------------------------------
+// E4M3 (OCP FP8) codes of 16 floats: the code nearest to x / scale (one IEEE
+// fp32 division each), ties to even.  The hardware convert rounds that way but
+// turns magnitudes from 464 up into NaN, so the quotient is clamped to +-448
+// first (saturation); a NaN quotient becomes code 0x7F.  Byte i of the result
+// holds element i.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, float scale) {
+  u32x4 out;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    float y[4];
+    uint32_t nan_mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q = x[4 * d + i] / scale;
+      nan_mask |= (q != q) ? (0xFFu << (8 * i)) : 0u;
+      y[i] = fminf(fmaxf(q, -448.f), 448.f);
+    }
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+    out[d] = (static_cast<uint32_t>(r) & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
+  }
+  return out;
+}
+
 }  // namespace pa

@@ -217,6 +217,53 @@ __device__ __forceinline__ void store_empty(const DecodeArgs& a, int b, int g) {
   }
 }
 
+// Append: store the new token's K and V (k_new/v_new row (b, g), the token at
+// position ctx-1) into its pool slot (block `phys`, offset `off`), then wait
+// until the stores have completed, so this wave's later loads of that block
+// see them.  Only the wave that reads position ctx-1 calls this, and no other
+// workgroup reads that row, so no wider ordering is needed.  Pool rows of
+// bf16/f32 are copied chunk by chunk (lanes 0 .. RC-1 K, RC .. 2RC-1 V); E4M3
+// rows take 16 elements per lane, quantised with the pool's scale.
+template <int D, int ESZ, bool KV8>
+__device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int g, int phys, int off, int lane) {
+  constexpr int RC = D * ESZ / 16;                      // source chunks per row
+  constexpr int PRC = KV8 ? D / 16 : RC;                // pool chunks per row
+  if (lane < 2 * PRC) {
+    const bool is_v = lane >= PRC;
+    const int c = is_v ? lane - PRC : lane;
+    const u32x4* src = static_cast<const u32x4*>(is_v ? a.v_new : a.k_new) +
+                       (static_cast<size_t>(b) * a.num_kv_heads + g) * RC;
+    u32x4* pool = const_cast<u32x4*>(static_cast<const u32x4*>(is_v ? a.v_cache : a.k_cache));
+    const size_t dst = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * a.block_size + off) * PRC + c;
+    if constexpr (KV8) {
+      float x[16];
+      const u32x4 w0 = src[2 * c], w1 = src[2 * c + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w0[i]);
+        x[2 * i + 1] = bf16_hi(w0[i]);
+        x[8 + 2 * i] = bf16_lo(w1[i]);
+        x[8 + 2 * i + 1] = bf16_hi(w1[i]);
+      }
+      pool[dst] = quantize16_e4m3(x, is_v ? a.v_scale[0] : a.k_scale[0]);
+    } else {
+      pool[dst] = src[c];
+    }
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
+// The block index of position ctx-1 if this wave of this work unit reads it
+// (and an append was asked for), else -1.
+__device__ __forceinline__ int append_block(const DecodeArgs& a, const Range& r, int wave, int W) {
+  if (a.k_new == nullptr || r.ctx <= 0) return -1;
+  const int lblk = (r.ctx - 1) / a.block_size;
+  if (lblk < r.blk_lo || lblk >= r.blk_hi || (lblk - r.blk_lo) % W != wave) return -1;
+  return lblk;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -245,6 +292,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int rg = lane / LPT, dl = lane % LPT;
   const int BS = a.block_size;
+  {
+    const int lblk = append_block(a, r, wave, 4);   // the waves take blocks round-robin
+    if (lblk >= 0) {
+      const int phys = a.block_tables[static_cast<size_t>(b) * a.max_blocks_per_seq + lblk];
+      if (phys >= 0 && phys < a.num_blocks) append_new_token<D, ESZ, false>(a, b, g, phys, (r.ctx - 1) % BS, lane);
+    }
+  }
 
   float qv[G][VEC];
   {
@@ -555,6 +609,13 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   if (r.blk_lo != ids_lo) {
     ids_lo = r.blk_lo;
     ids = load_ids(0);
+  }
+  {
+    const int lblk = append_block(a, r, wave, W);
+    if (lblk >= 0) {
+      const int phys = table[lblk];
+      if (phys >= 0 && phys < a.num_blocks) append_new_token<D, 2, KV8>(a, b, g, phys, (r.ctx - 1) % BS, lane);
+    }
   }
   const int span = r.blk_hi - r.blk_lo;
   const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;

@@ -83,6 +83,8 @@ struct DecodeArgs {
   int window;            // sliding window in keys (0 = none)
   const float* k_scale;  // E4M3 pools only: device scalars, value = code * scale
   const float* v_scale;
+  const void* k_new;     // append: [B, H_kv, d] K/V of the token at position ctx-1 (T),
+  const void* v_new;     //   stored into the pool by the kernel before it is read; else null
 };
 
 struct ReduceArgs {

@@ -35,10 +35,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
 }
 
 // E4M3 pools: every thread writes one 16-byte chunk of codes (16 elements of
-// a row).  A code is the E4M3 value nearest to x / scale (one IEEE fp32
-// division; bf16 inputs are widened exactly), ties to even: the hardware
-// convert rounds that way but turns magnitudes from 464 up into NaN, so the
-// quotient is clamped to +-448 first (saturation); NaN becomes code 0x7F.
+// a row, bf16 inputs widened exactly), quantised by quantize16_e4m3.
 template <bool BF>
 __global__ __launch_bounds__(256) void kv_write_fp8_kernel(KvWriteFp8Args a) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -74,21 +71,7 @@ __global__ __launch_bounds__(256) void kv_write_fp8_kernel(KvWriteFp8Args a) {
     }
   }
   const float scale = is_v ? a.v_scale[0] : a.k_scale[0];
-  u32x4 out;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    float y[4];
-    uint32_t nan_mask = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float q = x[4 * d + i] / scale;
-      nan_mask |= (q != q) ? (0xFFu << (8 * i)) : 0u;
-      y[i] = fminf(fmaxf(q, -448.f), 448.f);
-    }
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
-    out[d] = (static_cast<uint32_t>(r) & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
-  }
+  const u32x4 out = quantize16_e4m3(x, scale);
   u32x4* pool = is_v ? a.v_cache : a.k_cache;
   pool[dst] = out;
 }

@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
     "paged_attention_decode_fp8", "rope_cos_sin_cache", "paged_kv_write_rope",
+    "paged_attention_decode_append", "paged_attention_decode_append_fp8",
 )
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
 
@@ -83,6 +84,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                f32, vp, vp, i32, i32, vp]
+    lib.paged_attention_decode_append.restype = i32
+    lib.paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                  f32, i32, i32, vp]
+    lib.paged_attention_decode_append_fp8.restype = i32
+    lib.paged_attention_decode_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                      i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                      f32, vp, vp, i32, i32, vp]
     lib.rope_cos_sin_cache.restype = i32
     lib.rope_cos_sin_cache.argtypes = [vp, i32, i32, ctypes.c_double, vp]
     lib.paged_kv_write_rope.restype = i32
@@ -225,11 +234,14 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            lse: Optional[torch.Tensor] = None,
                            part_out: Optional[torch.Tensor] = None,
                            part_lse: Optional[torch.Tensor] = None, window: int = 0,
-                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None
+                           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                           k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None
                            ) -> Tuple[torch.Tensor, torch.Tensor]:
     """PagedAttention decode.  Returns (out, lse), or (part_out, part_lse) when split.
     window > 0 keeps only the last `window` positions (sliding window).  Pools of
-    uint8 / float8_e4m3fn hold E4M3 codes read with k_scale / v_scale."""
+    uint8 / float8_e4m3fn hold E4M3 codes read with k_scale / v_scale.  k_new /
+    v_new [B, H_kv, d]: the token at position ctx-1 of each sequence, stored into
+    the pools by the same launch before it is read (the step's cache write)."""
     lib = load_library()
     dt = _dtype_code(q)
     B, Hq, d = q.shape
@@ -267,7 +279,23 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             raise ValueError("paged_attention_decode: out/lse shape")
         po = _dev(out, "out", q.dtype)
         pl = _dev(lse, "lse", torch.float32)
-    if fp8:
+    if (k_new is None) != (v_new is None):
+        raise ValueError("paged_attention_decode: give both k_new and v_new, or neither")
+    if k_new is not None:
+        if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape or k_new.dtype != q.dtype or \
+                v_new.dtype != q.dtype:
+            raise ValueError("paged_attention_decode: k_new / v_new must be [B, H_kv, d] in q's dtype")
+        pkn, pvn = _dev(k_new, "k_new", ndim=3), _dev(v_new, "v_new", ndim=3)
+        if fp8:
+            _check(lib.paged_attention_decode_append_fp8(
+                po, pl, ppo, ppl, pq, pkn, pvn, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs, block_tables.shape[1], NB,
+                int(partition_size), int(max_context_len), float(scale), _scale_ptr(k_scale, "k_scale"),
+                _scale_ptr(v_scale, "v_scale"), int(window), dt, _stream(q)))
+        else:
+            _check(lib.paged_attention_decode_append(
+                po, pl, ppo, ppl, pq, pkn, pvn, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs, block_tables.shape[1], NB,
+                int(partition_size), int(max_context_len), float(scale), int(window), dt, _stream(q)))
+    elif fp8:
         _check(lib.paged_attention_decode_fp8(po, pl, ppo, ppl, pq, pkc, pvc, pbt, pcl, B, Hq, Hkv, d, bs,
                                               block_tables.shape[1], NB, int(partition_size),
                                               int(max_context_len), float(scale), _scale_ptr(k_scale, "k_scale"),

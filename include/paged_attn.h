@@ -312,6 +312,44 @@ int paged_attention_decode_fp8(void* out, float* lse, float* part_out, float* pa
                                pa_dtype dtype, void* stream);
 
 /*
+ * Decode with the step's cache write folded in.  A decode step writes each sequence's
+ * new token (paged_kv_write) and then attends over the cache including it; only the
+ * work unit that reads position ctx - 1 needs that row, so it stores it itself and waits
+ * for the stores before reading the block: one launch instead of two.
+ *
+ * paged_attention_decode_append - paged_attention_decode_window, except that k_new and
+ *   v_new ([num_seqs, num_kv_heads, head_dim], dtype) hold the K and V of the token at
+ *   position ctx - 1 of each sequence (ctx = context_lens[b]), which the call stores into
+ *   the pools at block block_tables[b][(ctx-1) / block_size], offset (ctx-1) % block_size
+ *   (exactly what paged_kv_write with that slot stores), before the attention reads it.
+ *   A sequence with ctx = 0 stores nothing; an out-of-range block id stores nothing.
+ *   The pools are written, so k_cache and v_cache are not const here.  Other arguments,
+ *   supported shapes and errors as paged_attention_decode_window.
+ *
+ * paged_attention_decode_append_fp8 - the same over E4M3 pools: the new rows are
+ *   quantised as paged_kv_write_fp8 quantises them (k_scale, v_scale), then the
+ *   attention is paged_attention_decode_fp8's.
+ */
+int paged_attention_decode_append(void* out, float* lse, float* part_out, float* part_lse,
+                                  const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int partition_size,
+                                  int max_context_len, float scale, int window, pa_dtype dtype,
+                                  void* stream);
+
+int paged_attention_decode_append_fp8(void* out, float* lse, float* part_out, float* part_lse,
+                                      const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, int partition_size,
+                                      int max_context_len, float scale, const float* k_scale,
+                                      const float* v_scale, int window, pa_dtype dtype,
+                                      void* stream);
+
+/*
  * Rotary position embedding fused into the cache write.  "LLaMA inference performance:
  * structure and source" (section 2.2, and step 1 of its attention listing) turns each
  * query and key vector by a position-dependent rotation computed from sin and cos, with

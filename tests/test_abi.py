@@ -184,3 +184,13 @@ def test_rope_validation(lib):
     assert call(P=0) == 1
     assert call(T=0) == 0
     assert call(dt=0, rot=20) == 2       # f32: 10 floats = 40 bytes, not whole chunks
+
+
+def test_append_validation(lib):
+    p = ctypes.c_void_p(16)
+    base = lambda kn=p, **kw: [p, p, p, p, p, kn, p, p, p, p, p, kw.get("B", 2), 32, 8, 128, 16, 8, 20, 0, 128, 0.1]
+    assert lib.paged_attention_decode_append(*base(kn=None), 0, 1, None) == 1        # k_new missing
+    assert lib.paged_attention_decode_append(*base(B=0), 0, 1, None) == 0            # nothing to do
+    assert lib.paged_attention_decode_append(*base(), -1, 1, None) == 1              # negative window
+    assert lib.paged_attention_decode_append_fp8(*base(kn=None), p, p, 0, 1, None) == 1
+    assert lib.paged_attention_decode_append_fp8(*base(), None, p, 0, 1, None) == 1  # null scale
