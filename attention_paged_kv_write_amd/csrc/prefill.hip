@@ -17,7 +17,9 @@
 // needs, so probabilities never move between lanes and each lane's softmax
 // state belongs to its own query column; V^T comes from the row-major tile by
 // ds_read_b64_tr_b16.  Key tiles past the diagonal are never visited; the mask
-// is applied on diagonal tiles only.
+// is applied on diagonal tiles only.  Q comes in and O goes out through LDS as
+// well, so that every global access moves whole 256-byte rows (a row per 16
+// lanes) instead of 32-64-byte pieces of 16 rows.
 //
 // Scheduling: workgroups are dealt to the 8 XCDs round-robin; the kernel maps
 // its id so that one head column (KV head, head block) stays on one XCD and
@@ -89,6 +91,8 @@ constexpr int kD = 128;
 
 // Wait until this wave's LDS-DMA loads have landed.
 __device__ __forceinline__ void wait_dma_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until this wave's LDS operations have completed.
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Max / sum over lanes l, l^16, l^32, l^48 (the four key quarters of a query
 // column) with VALU lane swaps.
@@ -331,33 +335,46 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int kt_cfull = wave_live ? (p_first + 1) >> 6 : 0;   // tiles below are causally full
   const int kt_last = wave_live ? p_last >> 6 : -1;
   const int kt0 = kmin >> 6;
-  load_ids(kt0, ids_cur);
-  issue(kt0, kvbuf + (kt0 & 1) * 2048);   // the first tile's loads overlap the Q loads
-  if (kt0 + 1 < nkt) load_ids(kt0 + 1, ids_next);
-
-  // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.  Rows past
-  // the sequence load its last row (all eight loads in flight at once) and are
-  // zeroed afterwards.
-  u32x4 qw[RG][4];
+  // Q rows of this wave go through LDS: the slot tile kt0 + 1 will use is free
+  // until after the first barrier, and a wave's 32 rows (8 KB) take a quarter
+  // of it.  Each DMA moves four whole 256-byte rows (16 lanes per row), and
+  // lane l of DMA i fetches chunk (l mod 16) ^ (row mod 16) so that the MFMA
+  // operand reads below are conflict-free.  Rows past the sequence load its
+  // last row and are zeroed afterwards.
+  {
+    u32x4* qbuf = kvbuf + ((kt0 + 1) & 1) * 2048 + wave * 512;
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int row = min(q0 + 16 * rg + c16, sp.len - 1);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qw[rg][c] = qc[(static_cast<size_t>(sp.start + row) * Hq + h) * RC + 4 * c + j];
-  }
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const bool live = q0 + 16 * rg + c16 < sp.len;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      qf[rg][c] = __builtin_bit_cast(bf16x8, live ? (qw[rg][c] ^ qsign) : zero);
+    for (int i = 0; i < 8; ++i) {
+      const int rl = 4 * i + (lane >> 4);
+      const int row = min(q0 + rl, sp.len - 1);
+      global_to_lds16(qc + (static_cast<size_t>(sp.start + row) * Hq + h) * RC + ((lane & 15) ^ (rl & 15)),
+                      &qbuf[64 * i]);
     }
   }
+  load_ids(kt0, ids_cur);
+  issue(kt0, kvbuf + (kt0 & 1) * 2048);
+  if (kt0 + 1 < nkt) load_ids(kt0 + 1, ids_next);
+  wait_dma_all();
+  __syncthreads();
+
+  // Q^T as B operands: rows q0 + 16rg + c16, dims 32c + 8j .. +7.
+  {
+    const u32x4* qbuf = kvbuf + ((kt0 + 1) & 1) * 2048 + wave * 512;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const bool live = q0 + 16 * rg + c16 < sp.len;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const u32x4 w = qbuf[(16 * rg + c16) * 16 + ((4 * c + j) ^ c16)];
+        qf[rg][c] = __builtin_bit_cast(bf16x8, live ? (w ^ qsign) : zero);
+      }
+    }
+  }
+  wait_lds_all();
+  __syncthreads();   // every wave holds its Q: the slot may be refilled
 
   for (int kt = kt0; kt < nkt; ++kt) {
-    wait_dma_all();
-    __syncthreads();
     if (kt + 1 < nkt) {
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) ids_cur[mm] = ids_next[mm];
@@ -369,25 +386,42 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     // within the register budget, which a skip-first form does not)
     if (kt >= kt_wfull && kt < kt_cfull) tile(kt, false);
     else if (kt >= kt_first && kt <= kt_last) tile(kt, true);
+    wait_dma_all();
+    __syncthreads();
   }
 
-  uint16_t* out = static_cast<uint16_t*>(a.out);
+  // O goes out through LDS as well (every wave is past its last tile read): the
+  // wave writes its 32 normalised rows into its own 8 KB (16-byte chunk k of
+  // row r at k ^ (r mod 16)), then stores four whole rows per instruction.
+  // (The lane index is made opaque here so that the compiler builds these
+  // addresses after the loop instead of holding them in registers through it.)
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int ej = el >> 4, e16 = el & 15;
+  u32x4* obuf = kvbuf + wave * 512;
+  char* obytes = reinterpret_cast<char*>(obuf);
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const float lt = quarter_reduce(l[rg], OpSum());
-    const int row = q0 + 16 * rg + c16;
-    if (row < sp.len) {
-      const float inv = 1.f / lt;
-      const size_t orow = static_cast<size_t>(sp.start + row) * Hq + h;
+    const int rl = 16 * rg + e16;
+    const float inv = 1.f / lt;
 #pragma unroll
-      for (int dn = 0; dn < 8; ++dn) {
-        u32x2 wo;
-        wo[0] = pack_bf16x2(oacc[rg][dn][0] * inv, oacc[rg][dn][1] * inv);
-        wo[1] = pack_bf16x2(oacc[rg][dn][2] * inv, oacc[rg][dn][3] * inv);
-        *reinterpret_cast<u32x2*>(out + orow * kD + 16 * dn + 4 * j) = wo;
-      }
-      if (j == 0) a.lse[orow] = (m[rg] + __log2f(lt)) * kLn2;
+    for (int dn = 0; dn < 8; ++dn) {
+      u32x2 wo;
+      wo[0] = pack_bf16x2(oacc[rg][dn][0] * inv, oacc[rg][dn][1] * inv);
+      wo[1] = pack_bf16x2(oacc[rg][dn][2] * inv, oacc[rg][dn][3] * inv);
+      *reinterpret_cast<u32x2*>(obytes + rl * 256 + 16 * ((2 * dn + (ej >> 1)) ^ e16) + 8 * (ej & 1)) = wo;
     }
+    const int row = q0 + rl;
+    if (ej == 0 && row < sp.len)
+      a.lse[static_cast<size_t>(sp.start + row) * Hq + h] = (m[rg] + __log2f(lt)) * kLn2;
+  }
+  u32x4* oc = static_cast<u32x4*>(a.out);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rl = 4 * i + ej;
+    const u32x4 w = obuf[rl * 16 + (e16 ^ (rl & 15))];
+    if (q0 + rl < sp.len) oc[(static_cast<size_t>(sp.start + q0 + rl) * Hq + h) * RC + e16] = w;
   }
 }
 
