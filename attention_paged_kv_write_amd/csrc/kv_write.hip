@@ -4,34 +4,65 @@
 // KV cache to FlashAttention", section 3.1, step 2) with a slot standing for
 // (physical block, offset) ("Llama 4 inference doubling (FlashAttention-3 +
 // PagedAttention + vLLM)", section 3.1).  A pure copy, so the kernel is an
-// HBM stream: every thread moves one 16-byte chunk of a row, consecutive
-// threads move consecutive chunks of the same token, so both the load from
-// k/v and the store into a (block, head) slab are contiguous runs of
-// head_dim * sizeof(T) bytes.
+// HBM stream: consecutive lanes move consecutive 16-byte chunks of the same
+// token, so both the load from k/v and the store into a (block, head) slab
+// are contiguous runs of head_dim * sizeof(T) bytes.
 #include "kernels.h"
 
 namespace pa {
 
+// Each wave copies the rows of kTokensPerWave consecutive tokens: the slot
+// lookup, its block / offset split and the row bases are wave-uniform
+// (scalar), and every lane keeps kChunkPasses x kTokensPerWave 16-byte loads
+// in flight before it stores them.  Lane l of pass k takes chunk 64k + l of a
+// token's K-then-V chunks, so a wave's loads and stores are contiguous runs.
+constexpr int kTokensPerWave = 4;
+constexpr int kChunkPasses = 4;
+
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_token = 2LL * a.row_chunks;  // K chunks then V chunks
-  if (item >= static_cast<int64_t>(a.num_tokens) * per_token) return;
-  const int t = static_cast<int>(item / per_token);
-  int c = static_cast<int>(item - static_cast<int64_t>(t) * per_token);
-  const bool is_v = c >= a.row_chunks;
-  if (is_v) c -= a.row_chunks;
-  const int slot = a.slot_mapping[t];
-  if (slot < 0 || static_cast<int64_t>(slot) >= a.num_slots) return;
-  const int h = c / a.head_chunks;
-  const int e = c - h * a.head_chunks;
-  const int blk = slot / a.block_size;
-  const int off = slot - blk * a.block_size;
-  const int64_t dst =
-      ((static_cast<int64_t>(blk) * a.num_kv_heads + h) * a.block_size + off) * a.head_chunks + e;
-  const int64_t src = static_cast<int64_t>(t) * a.row_chunks + c;
-  const u32x4* __restrict__ in = is_v ? a.v : a.k;
-  u32x4* __restrict__ pool = is_v ? a.v_cache : a.k_cache;
-  pool[dst] = __builtin_nontemporal_load(in + src);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + wave) * kTokensPerWave;
+  if (t0 >= a.num_tokens) return;
+  const int per_token = 2 * a.row_chunks;   // K chunks then V chunks
+  int64_t sbase[kTokensPerWave], dbase[kTokensPerWave];
+  bool live[kTokensPerWave];
+#pragma unroll
+  for (int i = 0; i < kTokensPerWave; ++i) {
+    const int t = t0 + i;
+    const int slot = t < a.num_tokens ? a.slot_mapping[t] : -1;
+    live[i] = slot >= 0 && static_cast<int64_t>(slot) < a.num_slots;
+    const int blk = live[i] ? slot / a.block_size : 0;
+    const int off = live[i] ? slot - blk * a.block_size : 0;
+    sbase[i] = static_cast<int64_t>(t) * a.row_chunks;
+    dbase[i] = (static_cast<int64_t>(blk) * a.num_kv_heads * a.block_size + off) * a.head_chunks;
+  }
+  const int head_stride = a.block_size * a.head_chunks;   // chunks from one head's slab to the next
+  for (int c00 = 0; c00 < per_token; c00 += 64 * kChunkPasses) {
+    u32x4 w[kChunkPasses][kTokensPerWave];
+    int doff[kChunkPasses];
+    bool isv[kChunkPasses], valid[kChunkPasses];
+#pragma unroll
+    for (int k = 0; k < kChunkPasses; ++k) {
+      const int c0 = c00 + 64 * k + lane;
+      valid[k] = c0 < per_token;
+      isv[k] = c0 >= a.row_chunks;
+      const int c = isv[k] ? c0 - a.row_chunks : c0;
+      const int h = c / a.head_chunks;
+      doff[k] = h * head_stride + (c - h * a.head_chunks);
+      const u32x4* __restrict__ in = isv[k] ? a.v : a.k;
+#pragma unroll
+      for (int i = 0; i < kTokensPerWave; ++i)
+        if (live[i] && valid[k]) w[k][i] = __builtin_nontemporal_load(in + sbase[i] + c);
+    }
+#pragma unroll
+    for (int k = 0; k < kChunkPasses; ++k) {
+      u32x4* __restrict__ pool = isv[k] ? a.v_cache : a.k_cache;
+#pragma unroll
+      for (int i = 0; i < kTokensPerWave; ++i)
+        if (live[i] && valid[k]) pool[dbase[i] + doff[k]] = w[k][i];
+    }
+  }
 }
 
 // E4M3 pools: every thread writes one 16-byte chunk of codes (16 elements of
@@ -88,9 +119,8 @@ hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t s
 }
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(a.num_tokens) * 2 * a.row_chunks;
-  if (items == 0) return hipSuccess;
-  const int64_t blocks = (items + 255) / 256;
+  if (a.num_tokens == 0 || a.row_chunks == 0) return hipSuccess;
+  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) + 4 * kTokensPerWave - 1) / (4 * kTokensPerWave);
   hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -283,13 +283,17 @@ def main(argv=None):
                            dtype=torch.bfloat16, device=dev)
         pool_v = torch.empty_like(pool)
         slots = up(pc.slot_mapping)
-        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b in wev:
-            a.record(stream)
+        # three warm-up writes, then HIP events on the launch stream around
+        # 20 back-to-back writes
+        for _ in range(3):
             ops.paged_kv_write(pk, pv, pool, pool_v, slots)
-            b.record(stream)
+        wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wa.record(stream)
+        for _ in range(20):
+            ops.paged_kv_write(pk, pv, pool, pool_v, slots)
+        wb.record(stream)
         torch.cuda.synchronize()
-        wms = float(np.mean([a.elapsed_time(b) for a, b in wev]))
+        wms = wa.elapsed_time(wb) / 20
         wbytes = 2 * 2 * pc.total_tokens * pc.spec.num_kv_heads * pc.spec.head_dim * 2  # read + write, K and V
         # RoPE fused into the prompt's cache write (row positions 0 .. L-1 of each
         # sequence, base 10000): q and k rotated in place, rotated k and v into
