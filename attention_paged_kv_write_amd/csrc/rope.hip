@@ -11,12 +11,13 @@
 // first half of a row, sin in the second) from fp64 angles, cos and sin, so
 // each entry is the exact value rounded once to fp32.
 //
-// rope_kv_write_kernel is one HBM pass over the step's rows: a thread owns
-// one 16-byte chunk of the first half of a rotated head row and the matching
-// chunk of the second half, turns them in fp32 with the table, stores them
-// back in place (q and k) and, for k, into the pool slot; v rows and the
-// dims past r are 16-byte copies into the pool.  Consecutive threads take
-// consecutive chunks of one head, so every load and store is a contiguous run.
+// rope_kv_write_kernel is one HBM pass over the step's rows: a lane owns one
+// 16-byte chunk of the first half of a rotated head row and the matching
+// chunk of the second half (of each of a few tokens), turns them in fp32 with
+// the table, stores them back in place (q and k) and, for k, into the pool
+// slot; v rows and the dims past r are 16-byte copies into the pool.
+// Consecutive lanes take consecutive chunks of one head, so every load and
+// store is a contiguous run.
 #include "kernels.h"
 
 namespace pa {
@@ -78,83 +79,118 @@ __device__ __forceinline__ u32x4 f32_to_chunk(const float* x) {
 
 // Items of a token, in order: q pairs (H_q x pair_chunks), k pairs (H_kv x
 // pair_chunks), k pass-through chunks (H_kv x (head_chunks - 2 pair_chunks)),
-// v chunks (H_kv x head_chunks).
+// v chunks (H_kv x head_chunks).  A wave takes kRopeTokensPerWave
+// consecutive tokens: their slot, position and block / offset split are
+// wave-uniform, lane l of pass k takes item 64k + l (its kind, head and chunk
+// computed once) and does it for each of the tokens, so every lane has that
+// many independent loads in flight.
+constexpr int kRopeTokensPerWave = 2;
+
 template <bool BF>
 __global__ __launch_bounds__(256) void rope_kv_write_kernel(RopeWriteArgs a) {
   constexpr int E = BF ? 8 : 4;   // elements per 16-byte chunk
+  constexpr int TPW = kRopeTokensPerWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + wave) * TPW;
+  if (t0 >= a.num_tokens) return;
   const int PC = a.pair_chunks, HC = a.head_chunks, TC = HC - 2 * PC;
   const int nq = a.num_q_heads * PC, nk = a.num_kv_heads * PC, nt = a.num_kv_heads * TC;
   const int per_token = nq + nk + nt + a.num_kv_heads * HC;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (item >= static_cast<int64_t>(a.num_tokens) * per_token) return;
-  const int t = static_cast<int>(item / per_token);
-  int c = static_cast<int>(item - static_cast<int64_t>(t) * per_token);
-  const int slot = a.slot_mapping[t];
-  const bool write = slot >= 0 && static_cast<int64_t>(slot) < a.num_slots;
-  const int blk = write ? slot / a.block_size : 0;
-  const int off = write ? slot - blk * a.block_size : 0;
-  auto pool_chunk = [&](int h, int e) -> int64_t {
-    return ((static_cast<int64_t>(blk) * a.num_kv_heads + h) * a.block_size + off) * HC + e;
-  };
+  const int half = a.rot_dim / 2;
 
-  if (c < nq + nk) {
-    const bool is_q = c < nq;
-    if (!is_q) c -= nq;
-    const int h = c / PC, e = c - h * PC;   // first-half chunk e, second-half chunk PC + e
-    const int H = is_q ? a.num_q_heads : a.num_kv_heads;
-    u32x4* row = static_cast<u32x4*>(is_q ? a.q : a.k) + (static_cast<int64_t>(t) * H + h) * HC;
-    const int p = clampi(a.positions[t], 0, a.max_positions - 1);   // out of range: unspecified, memory safe
-    const float* cs = a.cos_sin + static_cast<int64_t>(p) * a.rot_dim + e * E;
-    const int half = a.rot_dim / 2;
-    float x1[E], x2[E], c8[E], s8[E];
-    chunk_to_f32<BF>(row[e], x1);
-    chunk_to_f32<BF>(row[PC + e], x2);
+  bool live[TPW], write[TPW];
+  int64_t pbase[TPW];   // pool chunk of (block, head 0, offset, chunk 0)
+  int prow[TPW];        // table row (position; out of range: unspecified, memory safe)
 #pragma unroll
-    for (int i = 0; i < E; i += kF32PerChunk) {
-      const u32x4 cw = *reinterpret_cast<const u32x4*>(cs + i);
-      const u32x4 sw = *reinterpret_cast<const u32x4*>(cs + half + i);
+  for (int i = 0; i < TPW; ++i) {
+    const int t = t0 + i;
+    live[i] = t < a.num_tokens;
+    const int slot = live[i] ? a.slot_mapping[t] : -1;
+    write[i] = slot >= 0 && static_cast<int64_t>(slot) < a.num_slots;
+    const int blk = write[i] ? slot / a.block_size : 0;
+    const int off = write[i] ? slot - blk * a.block_size : 0;
+    pbase[i] = (static_cast<int64_t>(blk) * a.num_kv_heads * a.block_size + off) * HC;
+    prow[i] = live[i] ? clampi(a.positions[t], 0, a.max_positions - 1) : 0;
+  }
+  const int hstride = a.block_size * HC;   // pool chunks from one head's slab to the next
+
+  for (int c0 = lane; c0 < per_token; c0 += 64) {
+    if (c0 < nq + nk) {
+      const bool is_q = c0 < nq;
+      const int c = is_q ? c0 : c0 - nq;
+      const int h = c / PC, e = c - h * PC;   // first-half chunk e, second-half chunk PC + e
+      const int H = is_q ? a.num_q_heads : a.num_kv_heads;
+      u32x4* base = static_cast<u32x4*>(is_q ? a.q : a.k);
+      u32x4 r1[TPW], r2[TPW], cw[TPW][E / kF32PerChunk], sw[TPW][E / kF32PerChunk];
 #pragma unroll
-      for (int j = 0; j < kF32PerChunk; ++j) {
-        c8[i + j] = __uint_as_float(cw[j]);
-        s8[i + j] = __uint_as_float(sw[j]);
+      for (int i = 0; i < TPW; ++i) {
+        if (!live[i]) continue;
+        const u32x4* row = base + (static_cast<int64_t>(t0 + i) * H + h) * HC;
+        r1[i] = row[e];
+        r2[i] = row[PC + e];
+        const float* cs = a.cos_sin + static_cast<int64_t>(prow[i]) * a.rot_dim + e * E;
+#pragma unroll
+        for (int u = 0; u < E / kF32PerChunk; ++u) {
+          cw[i][u] = *reinterpret_cast<const u32x4*>(cs + u * kF32PerChunk);
+          sw[i][u] = *reinterpret_cast<const u32x4*>(cs + half + u * kF32PerChunk);
+        }
       }
-    }
-    float y1[E], y2[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      y1[i] = x1[i] * c8[i] - x2[i] * s8[i];
-      y2[i] = x2[i] * c8[i] + x1[i] * s8[i];
+      for (int i = 0; i < TPW; ++i) {
+        if (!live[i]) continue;
+        float x1[E], x2[E], y1[E], y2[E];
+        chunk_to_f32<BF>(r1[i], x1);
+        chunk_to_f32<BF>(r2[i], x2);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const float cv = __uint_as_float(cw[i][k / kF32PerChunk][k % kF32PerChunk]);
+          const float sv = __uint_as_float(sw[i][k / kF32PerChunk][k % kF32PerChunk]);
+          y1[k] = x1[k] * cv - x2[k] * sv;
+          y2[k] = x2[k] * cv + x1[k] * sv;
+        }
+        const u32x4 w1 = f32_to_chunk<BF>(y1), w2 = f32_to_chunk<BF>(y2);
+        u32x4* row = base + (static_cast<int64_t>(t0 + i) * H + h) * HC;
+        row[e] = w1;
+        row[PC + e] = w2;
+        if (!is_q && write[i]) {
+          a.k_cache[pbase[i] + h * hstride + e] = w1;
+          a.k_cache[pbase[i] + h * hstride + PC + e] = w2;
+        }
+      }
+    } else if (c0 < nq + nk + nt) {   // k dims past the rotated ones
+      const int c = c0 - nq - nk;
+      const int h = c / TC, e = 2 * PC + (c - h * TC);
+      const u32x4* kb = static_cast<const u32x4*>(a.k);
+      u32x4 w[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        if (write[i]) w[i] = kb[(static_cast<int64_t>(t0 + i) * a.num_kv_heads + h) * HC + e];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        if (write[i]) a.k_cache[pbase[i] + h * hstride + e] = w[i];
+    } else {
+      const int c = c0 - nq - nk - nt;
+      const int h = c / HC, e = c - h * HC;
+      const u32x4* vb = static_cast<const u32x4*>(a.v);
+      u32x4 w[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        if (write[i]) w[i] = __builtin_nontemporal_load(vb + (static_cast<int64_t>(t0 + i) * a.num_kv_heads + h) * HC + e);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        if (write[i]) a.v_cache[pbase[i] + h * hstride + e] = w[i];
     }
-    const u32x4 w1 = f32_to_chunk<BF>(y1), w2 = f32_to_chunk<BF>(y2);
-    row[e] = w1;
-    row[PC + e] = w2;
-    if (!is_q && write) {
-      a.k_cache[pool_chunk(h, e)] = w1;
-      a.k_cache[pool_chunk(h, PC + e)] = w2;
-    }
-    return;
   }
-  c -= nq + nk;
-  if (!write) return;
-  if (c < nt) {   // k dims past the rotated ones
-    const int h = c / TC, e = 2 * PC + (c - h * TC);
-    const u32x4* row = static_cast<const u32x4*>(a.k) + (static_cast<int64_t>(t) * a.num_kv_heads + h) * HC;
-    a.k_cache[pool_chunk(h, e)] = row[e];
-    return;
-  }
-  c -= nt;
-  const int h = c / HC, e = c - h * HC;
-  const u32x4* row = static_cast<const u32x4*>(a.v) + (static_cast<int64_t>(t) * a.num_kv_heads + h) * HC;
-  a.v_cache[pool_chunk(h, e)] = __builtin_nontemporal_load(row + e);
 }
 
 hipError_t launch_rope_kv_write(const RopeWriteArgs& a, DType dt, hipStream_t stream) {
   const int64_t per_token = static_cast<int64_t>(a.num_q_heads) * a.pair_chunks +
                             static_cast<int64_t>(a.num_kv_heads) * (a.head_chunks - a.pair_chunks) +
                             static_cast<int64_t>(a.num_kv_heads) * a.head_chunks;
-  const int64_t items = static_cast<int64_t>(a.num_tokens) * per_token;
-  if (items == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  if (a.num_tokens == 0 || per_token == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(a.num_tokens) + 4 * kRopeTokensPerWave - 1) /
+                                        (4 * kRopeTokensPerWave)));
   if (dt == DType::BF16)
     hipLaunchKernelGGL(rope_kv_write_kernel<true>, grid, dim3(256), 0, stream, a);
   else

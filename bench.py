@@ -308,13 +308,13 @@ def main(argv=None):
         for _ in range(3):
             ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
         torch.cuda.synchronize()
-        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b in rev:
-            a.record(stream)
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ra.record(stream)
+        for _ in range(20):
             ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
-            b.record(stream)
+        rb.record(stream)
         torch.cuda.synchronize()
-        rms = float(np.mean([a.elapsed_time(b) for a, b in rev]))
+        rms = ra.elapsed_time(rb) / 20
         rgbs = rope_bytes / (rms * 1e-3) / 1e9
         rope_write = {"workload": pc.spec.name + " prompt rows", "rot_dim": d_, "base": 10000.0,
                       "kernel_avg_us": round(rms * 1e3, 1),
