@@ -11,24 +11,27 @@
 
 namespace pa {
 
-// Each wave copies the rows of kTokensPerWave consecutive tokens: the slot
-// lookup, its block / offset split and the row bases are wave-uniform
-// (scalar), and every lane keeps kChunkPasses x kTokensPerWave 16-byte loads
-// in flight before it stores them.  Lane l of pass k takes chunk 64k + l of a
-// token's K-then-V chunks, so a wave's loads and stores are contiguous runs.
-constexpr int kTokensPerWave = 4;
-constexpr int kChunkPasses = 4;
-
+// A wave copies TPW consecutive tokens' rows, KP passes of 64 chunks each:
+// the slot lookup, its block / offset split and the row bases are
+// wave-uniform (scalar), lane l of pass k takes chunk 64k + l of a token's
+// K-then-V chunks (so a wave's loads and stores are contiguous runs), and
+// every lane issues its KP x TPW 16-byte loads before it stores them.  Waves
+// are numbered token group major, pass group minor.  Large writes use 4 x 4
+// (16 loads in flight per lane); small ones 1 x 1, so that a few tokens
+// still spread over many CUs.
+template <int TPW, int KP>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * 4 + wave) * kTokensPerWave;
-  if (t0 >= a.num_tokens) return;
   const int per_token = 2 * a.row_chunks;   // K chunks then V chunks
-  int64_t sbase[kTokensPerWave], dbase[kTokensPerWave];
-  bool live[kTokensPerWave];
+  const int npg = (per_token + 64 * KP - 1) / (64 * KP);   // pass groups per token group
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  const int grp = w / npg, pg = w - grp * npg;
+  const int t0 = grp * TPW;
+  if (t0 >= a.num_tokens) return;
+  int64_t sbase[TPW], dbase[TPW];
+  bool live[TPW];
 #pragma unroll
-  for (int i = 0; i < kTokensPerWave; ++i) {
+  for (int i = 0; i < TPW; ++i) {
     const int t = t0 + i;
     const int slot = t < a.num_tokens ? a.slot_mapping[t] : -1;
     live[i] = slot >= 0 && static_cast<int64_t>(slot) < a.num_slots;
@@ -38,30 +41,29 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     dbase[i] = (static_cast<int64_t>(blk) * a.num_kv_heads * a.block_size + off) * a.head_chunks;
   }
   const int head_stride = a.block_size * a.head_chunks;   // chunks from one head's slab to the next
-  for (int c00 = 0; c00 < per_token; c00 += 64 * kChunkPasses) {
-    u32x4 w[kChunkPasses][kTokensPerWave];
-    int doff[kChunkPasses];
-    bool isv[kChunkPasses], valid[kChunkPasses];
+  const int c00 = pg * 64 * KP;
+  u32x4 w16[KP][TPW];
+  int doff[KP];
+  bool isv[KP], valid[KP];
 #pragma unroll
-    for (int k = 0; k < kChunkPasses; ++k) {
-      const int c0 = c00 + 64 * k + lane;
-      valid[k] = c0 < per_token;
-      isv[k] = c0 >= a.row_chunks;
-      const int c = isv[k] ? c0 - a.row_chunks : c0;
-      const int h = c / a.head_chunks;
-      doff[k] = h * head_stride + (c - h * a.head_chunks);
-      const u32x4* __restrict__ in = isv[k] ? a.v : a.k;
+  for (int k = 0; k < KP; ++k) {
+    const int c0 = c00 + 64 * k + lane;
+    valid[k] = c0 < per_token;
+    isv[k] = c0 >= a.row_chunks;
+    const int c = isv[k] ? c0 - a.row_chunks : c0;
+    const int h = c / a.head_chunks;
+    doff[k] = h * head_stride + (c - h * a.head_chunks);
+    const u32x4* __restrict__ in = isv[k] ? a.v : a.k;
 #pragma unroll
-      for (int i = 0; i < kTokensPerWave; ++i)
-        if (live[i] && valid[k]) w[k][i] = __builtin_nontemporal_load(in + sbase[i] + c);
-    }
+    for (int i = 0; i < TPW; ++i)
+      if (live[i] && valid[k]) w16[k][i] = __builtin_nontemporal_load(in + sbase[i] + c);
+  }
 #pragma unroll
-    for (int k = 0; k < kChunkPasses; ++k) {
-      u32x4* __restrict__ pool = isv[k] ? a.v_cache : a.k_cache;
+  for (int k = 0; k < KP; ++k) {
+    u32x4* __restrict__ pool = isv[k] ? a.v_cache : a.k_cache;
 #pragma unroll
-      for (int i = 0; i < kTokensPerWave; ++i)
-        if (live[i] && valid[k]) pool[dbase[i] + doff[k]] = w[k][i];
-    }
+    for (int i = 0; i < TPW; ++i)
+      if (live[i] && valid[k]) pool[dbase[i] + doff[k]] = w16[k][i];
   }
 }
 
@@ -120,8 +122,18 @@ hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t s
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0 || a.row_chunks == 0) return hipSuccess;
-  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) + 4 * kTokensPerWave - 1) / (4 * kTokensPerWave);
-  hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+  const int64_t passes = (2LL * a.row_chunks + 63) / 64;   // 64-chunk passes per token
+  auto waves = [&](int tpw, int kp) {
+    return (static_cast<int64_t>(a.num_tokens) + tpw - 1) / tpw * ((passes + kp - 1) / kp);
+  };
+  if (a.num_tokens >= 4096) {
+    const int64_t blocks = (waves(4, 4) + 3) / 4;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kv_write_kernel<4, 4>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+  } else {
+    const int64_t blocks = (waves(1, 1) + 3) / 4;
+    hipLaunchKernelGGL((kv_write_kernel<1, 1>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -77,6 +77,42 @@ def test_kv_write_bit_exact(name):
     assert to_host_bits(vc).tobytes() == ev.tobytes()
 
 
+# Layouts of the write kernel (a wave per one or four tokens, lanes over a
+# token's K-then-V chunks in passes of 64): more than one 256-chunk pass per
+# token, a head of 3 chunks and a block of 5 slots (no powers of two), a chunk
+# count below one wave, token counts that leave waves partly empty, skipped
+# slots.
+WRITE_LAYOUTS = {
+    "bf16_h20_d128_bs16_T37": (wl.BF16, 37, 20, 128, 16, 60),
+    "bf16_h3_d24_bs5_T5": (wl.BF16, 5, 3, 24, 5, 4),
+    "f32_h1_d64_bs16_T33": (wl.F32, 33, 1, 64, 16, 5),
+    "f32_h6_d8_bs3_T18": (wl.F32, 18, 6, 8, 3, 9),
+    # past 4096 tokens the kernel takes four tokens and four passes per wave
+    "bf16_h3_d24_bs5_T4099": (wl.BF16, 4099, 3, 24, 5, 1000),
+    "bf16_h20_d128_bs16_T4100": (wl.BF16, 4100, 20, 128, 16, 300),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WRITE_LAYOUTS))
+def test_kv_write_layouts_bit_exact(name):
+    dtype, T, H, d, bs, nb = WRITE_LAYOUTS[name]
+    rng = np.random.default_rng(77)
+    k = wl.f32_to_bf16_bits(rng.standard_normal((T, H, d), np.float32)) if dtype == wl.BF16 \
+        else rng.standard_normal((T, H, d)).astype(np.float32)
+    v = wl.f32_to_bf16_bits(rng.standard_normal((T, H, d), np.float32)) if dtype == wl.BF16 \
+        else rng.standard_normal((T, H, d)).astype(np.float32)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int32)
+    slots[rng.random(T) < 0.2] = -1
+    pk = wl.empty_pool(nb, H, bs, d, dtype)
+    pv = pk.copy()
+    kc, vc = to_dev(pk), to_dev(pv)
+    ops.paged_kv_write(to_dev(k), to_dev(v), kc, vc, to_dev(slots))
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_write(pk, pv, k, v, slots, bs)
+    assert to_host_bits(kc).tobytes() == ek.tobytes()
+    assert to_host_bits(vc).tobytes() == ev.tobytes()
+
+
 def test_kv_write_prefill_pool_bit_exact():
     case = wl.make_case(3)
     spec = case.spec
