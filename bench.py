@@ -517,6 +517,19 @@ def main(argv=None):
                      lse=torch.empty((fB, fHq), dtype=torch.float32, device=dev))
             ops.paged_kv_write(fk_all, fv_all, c["kc"], c["vc"], fslots, k_scale=ks_d, v_scale=vs_d)
             fcopies.append(c)
+        # the quantising write of the whole history (bf16 rows in, E4M3 codes out),
+        # rewritten into the first copy's pools (same values): HIP events around
+        # 10 back-to-back writes after one warm-up
+        ops.paged_kv_write(fk_all, fv_all, fcopies[0]["kc"], fcopies[0]["vc"], fslots, k_scale=ks_d, v_scale=vs_d)
+        hwa, hwb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hwa.record(stream)
+        for _ in range(10):
+            ops.paged_kv_write(fk_all, fv_all, fcopies[0]["kc"], fcopies[0]["vc"], fslots, k_scale=ks_d, v_scale=vs_d)
+        hwb.record(stream)
+        torch.cuda.synchronize()
+        fw_ms = hwa.elapsed_time(hwb) / 10
+        fw_tokens = int(fk_all.shape[0])
+        fw_bytes = fw_tokens * fHkv * fd * 2 * 3   # K and V: 2 bytes read, 1 byte written per element
         del fk_all, fv_all
 
         def fdecode(c):
@@ -552,6 +565,10 @@ def main(argv=None):
                "sum_context": int(fc.context_lens.sum()), "kv_bytes_per_step": fbytes,
                "step_us": round(fsms * 1e3, 2), "step_gbs": round(fbytes / (fsms * 1e-3) / 1e9, 1),
                "decode_tokens_per_s": round(fB / (fsms * 1e-3), 1),
+               "history_write": {"tokens": fw_tokens, "kernel_avg_us": round(fw_ms * 1e3, 1),
+                                 "gbs": round(fw_bytes / (fw_ms * 1e-3) / 1e9, 1),
+                                 "kernel": "kv_write_fp8_kernel<bf16> (paged_kv_write_fp8)",
+                                 "bound": "fp32 IEEE divisions of the quantiser (16 per 16-byte chunk of codes)"},
                "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(fgbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(FP8_TRAFFIC_FILE, DECODE_SOURCES),
@@ -559,7 +576,8 @@ def main(argv=None):
                             "kernel_avg_us": round(favg * 1e3, 2),
                             "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
                             "algorithmic_bytes_per_launch": fbytes}}
-        log(f"fp8 decode kernel {favg * 1e3:.1f} us -> {fgbs:.0f} GB/s of E4M3 KV; step {fsms * 1e3:.1f} us")
+        log(f"fp8 decode kernel {favg * 1e3:.1f} us -> {fgbs:.0f} GB/s of E4M3 KV; step {fsms * 1e3:.1f} us; "
+            f"history write ({fw_tokens} tokens) {fw_ms * 1e3:.1f} us -> {fw_bytes / (fw_ms * 1e-3) / 1e9:.0f} GB/s")
         del fcopies
         torch.cuda.empty_cache()
 
