@@ -260,10 +260,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[nt][i] = sacc[nt][rg][i] * sl2;
-          if (masked && static_cast<unsigned>(d - (16 * nt + i)) >= wlim) sv[nt][i] = kNegInf;
-        }
+        for (int i = 0; i < 4; ++i) sv[nt][i] = sacc[nt][rg][i] * sl2;
+      if (masked) {
+        // (opaque, so that the compares are not hoisted into unmasked tiles)
+        int dm = d;
+        asm volatile("" : "+v"(dm));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (static_cast<unsigned>(dm - (16 * nt + i)) >= wlim) sv[nt][i] = kNegInf;
+      }
       float mx = vmax3(vmax3(sv[0][0], sv[0][1], sv[0][2]), vmax3(sv[0][3], sv[1][0], sv[1][1]),
                        vmax3(sv[1][2], sv[1][3], sv[2][0]));
       mx = vmax3(mx, vmax3(sv[2][1], sv[2][2], sv[2][3]), vmax3(sv[3][0], sv[3][1], vmax3(sv[3][2], sv[3][3], sv[3][3])));
@@ -384,8 +391,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     // (kt_wfull >= kt_first and kt_cfull <= kt_last + 1, so the unmasked range
     // lies inside the visible one; this form of the test also keeps the loop
     // within the register budget, which a skip-first form does not)
-    if (kt >= kt_wfull && kt < kt_cfull) tile(kt, false);
-    else if (kt >= kt_first && kt <= kt_last) tile(kt, true);
+    // One tile body for both kinds (the mask is a wave-uniform branch over the
+    // scores only): two inlined bodies made the compiler copy all of O between
+    // registers at every iteration.
+    if (kt >= kt_first && kt <= kt_last) tile(kt, !(kt >= kt_wfull && kt < kt_cfull));
     wait_dma_all();
     __syncthreads();
   }
