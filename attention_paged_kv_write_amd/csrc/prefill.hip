@@ -155,7 +155,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // Scores are reduced unscaled; a negative scale is folded into Q (exact
   // sign flip of the bf16 values) so the max of raw scores is the max of
   // scaled ones.
-  const float sl2 = fabsf(a.scale_log2);
+  // (a zero scale becomes the smallest normal float: every score times it
+  // still rounds to nothing in the exponent, and masked keys stay -inf
+  // instead of -inf * 0 = NaN)
+  const float sl2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   bf16x8 qf[RG][4];   // Q^T B operands, loaded below (after the first tile is requested)
@@ -252,6 +255,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       // scaled scores (log2 units).  The multiply also hands the matrix-core
       // results to the vector ALU under the compiler's hazard tracking before
       // the inline-asm max reads them.
+      // Raw scores: the scale (positive here) is applied after the max,
+      // max(s) * scale == max(s * scale) exactly, and inside the exponent's
+      // FMA.  The max is IEEE maximum (v_maximum3_f32), which the compiler
+      // builds without NaN-quieting copies and whose reads of the matrix-core
+      // results it orders itself.
       float sv[4][4];
       // The row's position (among the keys) minus this lane's first key of the
       // tile, kt*64 + 4j: key kt*64 + 4j + 16nt + i is visible iff
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[nt][i] = sacc[nt][rg][i] * sl2;
+        for (int i = 0; i < 4; ++i) sv[nt][i] = sacc[nt][rg][i];
       if (masked) {
         // (opaque, so that the compares are not hoisted into unmasked tiles)
         int dm = d;
@@ -271,10 +279,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
           for (int i = 0; i < 4; ++i)
             if (static_cast<unsigned>(dm - (16 * nt + i)) >= wlim) sv[nt][i] = kNegInf;
       }
-      float mx = vmax3(vmax3(sv[0][0], sv[0][1], sv[0][2]), vmax3(sv[0][3], sv[1][0], sv[1][1]),
-                       vmax3(sv[1][2], sv[1][3], sv[2][0]));
-      mx = vmax3(mx, vmax3(sv[2][1], sv[2][2], sv[2][3]), vmax3(sv[3][0], sv[3][1], vmax3(sv[3][2], sv[3][3], sv[3][3])));
-      mx = quarter_max(mx);
+      auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+      float mx = mx2(mx2(mx2(mx2(sv[0][0], sv[0][1]), mx2(sv[0][2], sv[0][3])),
+                         mx2(mx2(sv[1][0], sv[1][1]), mx2(sv[1][2], sv[1][3]))),
+                     mx2(mx2(mx2(sv[2][0], sv[2][1]), mx2(sv[2][2], sv[2][3])),
+                         mx2(mx2(sv[3][0], sv[3][1]), mx2(sv[3][2], sv[3][3]))));
+      mx = quarter_max(mx) * sl2;
       // lazy rescale: the whole wave moves its maxima only when some row's
       // max has grown past the slack.  A row with no visible key in a masked
       // tile has mx = -inf and keeps its m, which stays -inf until the row's
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       for (int nt = 0; nt < 4; ++nt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[nt][i] - ms);   // masked: exp2(-inf) = 0
+        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(fmaf(sv[nt][i], sl2, -ms));   // masked: exp2(-inf) = 0
         ps[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
         pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
