@@ -191,6 +191,25 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     }
   };
   auto issue = [&](int kt, u32x4* buf) {
+    if constexpr (!PAGED) {
+      if (kt * kPN >= kmin && kt * kPN + kPN <= ks.ctx) {
+        // The whole tile lies inside the sequence: one wave-uniform base and
+        // a 32-bit offset per lane (scalar base + vector offset addressing,
+        // no 64-bit address arithmetic per load).  The lane part is opaque so
+        // that it is not hoisted out of the key loop as 64-bit addresses.
+        const size_t t0 = (static_cast<size_t>(sp.start + kt * kPN) * Hkv + g) * RC;
+        const char* kb = reinterpret_cast<const char*>(kc + t0);
+        const char* vb = reinterpret_cast<const char*>(vc + t0);
+        uint32_t lo0 = static_cast<uint32_t>(drow * Hkv * RC * 16);
+        asm volatile("" : "+v"(lo0));
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const uint32_t off = lo0 + static_cast<uint32_t>((16 * (ii & 3) * Hkv * RC + (ii < 4 ? kchunk : vchunk)) * 16);
+          global_to_lds16((ii < 4 ? kb : vb) + off, &buf[64 * (wave + 4 * ii)]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) {
       const int row = drow + 16 * (ii & 3);
