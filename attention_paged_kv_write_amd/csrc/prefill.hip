@@ -184,13 +184,41 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   const int32_t* table = PAGED ? a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq : nullptr;
   const int lbs = PAGED ? __builtin_ctz(a.block_size) : 0;
   int ids_cur[4] = {0, 0, 0, 0}, ids_next[4] = {0, 0, 0, 0};
+  // A whole tile (no clamped key) with blocks of at least 16 keys: each DMA
+  // slice of 16 rows lies in one block, so its table entry is wave-uniform
+  // (a scalar load) and the lane's part of the address is a constant 32-bit
+  // offset.  Other tiles take per-lane table entries.
+  auto whole_tile = [&](int kt) { return kt * kPN >= kmin && kt * kPN + kPN <= ks.ctx; };
+  const bool uniform_blocks = PAGED && a.block_size >= 16;
   auto load_ids = [&](int kt, int (&ids)[4]) {
     if constexpr (PAGED) {
+      if (uniform_blocks && whole_tile(kt)) {
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) ids[mm] = table[min(max(kt * kPN + drow + 16 * mm, kmin), ks.ctx - 1) >> lbs];
+        for (int mm = 0; mm < 4; ++mm) ids[mm] = table[(kt * kPN + 16 * mm) >> lbs];
+      } else {
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) ids[mm] = table[min(max(kt * kPN + drow + 16 * mm, kmin), ks.ctx - 1) >> lbs];
+      }
     }
   };
   auto issue = [&](int kt, u32x4* buf) {
+    if constexpr (PAGED) {
+      if (uniform_blocks && whole_tile(kt)) {
+        uint32_t lo0 = static_cast<uint32_t>(drow * RC * 16);
+        asm volatile("" : "+v"(lo0));
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int mm = ii & 3;
+          int phys = __builtin_amdgcn_readfirstlane(ids_cur[mm]);
+          phys = (phys >= 0 && phys < a.num_blocks) ? phys : 0;   // bad ids read block 0 (result unspecified)
+          const size_t base = ((static_cast<size_t>(phys) * Hkv + g) * a.block_size +
+                               ((kt * kPN + 16 * mm) & (a.block_size - 1))) * RC;
+          const char* src = reinterpret_cast<const char*>((ii < 4 ? kc : vc) + base);
+          global_to_lds16(src + lo0 + static_cast<uint32_t>((ii < 4 ? kchunk : vchunk) * 16), &buf[64 * (wave + 4 * ii)]);
+        }
+        return;
+      }
+    }
     if constexpr (!PAGED) {
       if (kt * kPN >= kmin && kt * kPN + kPN <= ks.ctx) {
         // The whole tile lies inside the sequence: one wave-uniform base and
