@@ -299,9 +299,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
     bf16x8 pf[2][RG];   // P^T B operands: [key chunk of 32][rg]
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      // scaled scores (log2 units).  The multiply also hands the matrix-core
-      // results to the vector ALU under the compiler's hazard tracking before
-      // the inline-asm max reads them.
       // Raw scores: the scale (positive here) is applied after the max,
       // max(s) * scale == max(s * scale) exactly, and inside the exponent's
       // FMA.  The max is IEEE maximum (v_maximum3_f32), which the compiler
