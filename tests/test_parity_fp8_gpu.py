@@ -2,7 +2,7 @@
 
 The write is compared bit for bit on whole pools: random rows, quotients a
 few ulps either side of every rounding midpoint, saturating magnitudes, NaN,
-skipped slots.  Decode reads a pool the GPU wrote itself and is compared with
+skipped slots, and every bf16 bit pattern at five scales.  Decode reads a pool the GPU wrote itself and is compared with
 the oracle's attention over the pool the oracle wrote (the two pools are
 first checked identical): single pass, split with the window-aware merge,
 sliding window, four group / block-size shapes, and the FP8 Llama-3-8B decode
@@ -78,6 +78,25 @@ def test_kv_write_fp8_bit_exact(dtype):
     okc, ovc = oracle.kv_write_fp8(kc, vc, k, v, slots, bs, dtype, ks, vs)
     dkc, dvc = to_dev(kc), to_dev(vc)
     ops.paged_kv_write(to_dev(k), to_dev(v), dkc, dvc, to_dev(slots), k_scale=scale_dev(ks), v_scale=scale_dev(vs))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dkc.cpu().numpy(), okc)
+    np.testing.assert_array_equal(dvc.cpu().numpy(), ovc)
+
+
+@pytest.mark.parametrize("scale", [6 / 448, 0.37, 1.0, 3e-3, 1e4])
+def test_kv_write_fp8_every_bf16_value(scale):
+    # every bf16 bit pattern (NaNs, infinities, subnormals, both zeros) as K and
+    # as V, in 512 tokens of one 128-dim head: whole pools bit-exact
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(512, 1, 128)
+    k, v = bits, bits[::-1].copy()
+    slots = np.random.default_rng(43).permutation(512).astype(np.int32)
+    kc = np.zeros((32, 1, 16, 128), np.uint8)
+    vc = kc.copy()
+    sc = np.float32(scale)
+    with np.errstate(invalid="ignore", over="ignore"):   # NaN and infinite inputs are part of the sweep
+        okc, ovc = oracle.kv_write_fp8(kc, vc, k, v, slots, 16, wl.BF16, sc, sc)
+    dkc, dvc = to_dev(kc), to_dev(vc)
+    ops.paged_kv_write(to_dev(k), to_dev(v), dkc, dvc, to_dev(slots), k_scale=scale_dev(sc), v_scale=scale_dev(sc))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(dkc.cpu().numpy(), okc)
     np.testing.assert_array_equal(dvc.cpu().numpy(), ovc)
