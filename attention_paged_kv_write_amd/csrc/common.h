@@ -147,13 +147,43 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 (OCP FP8) codes of 16 floats: the code nearest to x / scale (one IEEE
-// fp32 division each), ties to even.  The hardware convert rounds that way but
-// turns magnitudes from 464 up into NaN, so the quotient is clamped to +-448
-// first (saturation); a NaN quotient becomes code 0x7F.  Byte i of the result
-// holds element i.
+// Division by a per-pool scale s, correctly rounded.  The steps are those the
+// compiler emits for an IEEE fp32 division (a reciprocal refined once, then
+// two residual corrections), with the reciprocal built once per scale and
+// without the operand scaling and result fix-up steps, which change nothing
+// while |s| lies in [2^-30, 2^30] and the quotient is a normal number below
+// 2^20.  A larger first product (an infinite numerator, an overflowing
+// quotient) is kept as it is: the +-448 clamp that follows saturates it the
+// same way.  The sign is taken from the first product, so a zero keeps its
+// sign.  Other scales divide.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, float scale) {
+struct ScaleRcp {
+  float s, r;
+  bool fast;
+};
+
+__device__ __forceinline__ ScaleRcp scale_rcp(float s) {
+  const float a = fabsf(s);
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return ScaleRcp{s, fmaf(fmaf(-s, r0, 1.f), r0, r0), a >= 0x1p-30f && a <= 0x1p30f};
+}
+
+__device__ __forceinline__ float div_by_scale(float x, const ScaleRcp& sr) {
+  const float q0 = x * sr.r;
+  float q = fmaf(fmaf(-sr.s, q0, x), sr.r, q0);
+  q = fmaf(fmaf(-sr.s, q, x), sr.r, q);
+  q = fabsf(q0) > 1.0e6f ? q0 : q;
+  return copysignf(q, q0);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP FP8) codes of 16 floats: the code nearest to x / scale (the
+// correctly rounded fp32 quotient), ties to even.  The hardware convert rounds
+// that way but turns magnitudes from 464 up into NaN, so the quotient is
+// clamped to +-448 first (saturation); a NaN quotient becomes code 0x7F.  Byte
+// i of the result holds element i.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 e4m3_codes16(const float* q16) {
   u32x4 out;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -161,7 +191,7 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, float scale) {
     uint32_t nan_mask = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float q = x[4 * d + i] / scale;
+      const float q = q16[4 * d + i];
       nan_mask |= (q != q) ? (0xFFu << (8 * i)) : 0u;
       y[i] = fminf(fmaxf(q, -448.f), 448.f);
     }
@@ -170,6 +200,22 @@ __device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, float scale) {
     out[d] = (static_cast<uint32_t>(r) & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
   }
   return out;
+}
+
+__device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, const ScaleRcp& sr) {
+  float q[16];
+  if (sr.fast) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = div_by_scale(x[i], sr);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = x[i] / sr.s;
+  }
+  return e4m3_codes16(q);
+}
+
+__device__ __forceinline__ u32x4 quantize16_e4m3(const float* x, float scale) {
+  return quantize16_e4m3(x, scale_rcp(scale));
 }
 
 }  // namespace pa

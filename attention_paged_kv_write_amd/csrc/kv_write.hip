@@ -67,52 +67,57 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   }
 }
 
-// E4M3 pools: every thread writes one 16-byte chunk of codes (16 elements of
-// a row, bf16 inputs widened exactly), quantised by quantize16_e4m3.
+// E4M3 pools: a lane writes one 16-byte chunk of codes (16 elements of a
+// row, bf16 inputs widened exactly), quantised by quantize16_e4m3.  Waves are
+// laid out as in kv_write_kernel with one token and one 64-chunk pass each, so
+// that every lane has its own chunk: the quantiser's arithmetic, not memory,
+// bounds this kernel.
 template <bool BF>
 __global__ __launch_bounds__(256) void kv_write_fp8_kernel(KvWriteFp8Args a) {
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_token = 2LL * a.row_chunks;  // K chunks then V chunks
-  if (item >= static_cast<int64_t>(a.num_tokens) * per_token) return;
-  const int t = static_cast<int>(item / per_token);
-  int c = static_cast<int>(item - static_cast<int64_t>(t) * per_token);
-  const bool is_v = c >= a.row_chunks;
-  if (is_v) c -= a.row_chunks;
+  constexpr int SRC_CHUNKS = BF ? 2 : 4;   // 16 source elements: 2 (bf16) or 4 (f32) 16-byte chunks
+  const int lane = threadIdx.x & 63;
+  const int per_token = 2 * a.row_chunks;   // K chunks then V chunks (of codes)
+  const int npass = (per_token + 63) / 64;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  const int t = w / npass, pass = w - t * npass;
+  if (t >= a.num_tokens) return;
   const int slot = a.slot_mapping[t];
   if (slot < 0 || static_cast<int64_t>(slot) >= a.num_slots) return;
+  const int c0 = pass * 64 + lane;
+  if (c0 >= per_token) return;
+  const bool is_v = c0 >= a.row_chunks;
+  const int c = is_v ? c0 - a.row_chunks : c0;
   const int h = c / a.head_chunks;
   const int e = c - h * a.head_chunks;
   const int blk = slot / a.block_size;
   const int off = slot - blk * a.block_size;
-  const int64_t dst =
-      ((static_cast<int64_t>(blk) * a.num_kv_heads + h) * a.block_size + off) * a.head_chunks + e;
-  // 16 source elements: 2 (bf16) or 4 (f32) 16-byte chunks
-  constexpr int SRC_CHUNKS = BF ? 2 : 4;
+  const int64_t dst = ((static_cast<int64_t>(blk) * a.num_kv_heads + h) * a.block_size + off) * a.head_chunks + e;
   const u32x4* in = static_cast<const u32x4*>(is_v ? a.v : a.k) +
                     (static_cast<int64_t>(t) * a.row_chunks + c) * SRC_CHUNKS;
-  u32x4 w[SRC_CHUNKS];
+  u32x4 w4[SRC_CHUNKS];
 #pragma unroll
-  for (int i = 0; i < SRC_CHUNKS; ++i) w[i] = __builtin_nontemporal_load(in + i);
+  for (int i = 0; i < SRC_CHUNKS; ++i) w4[i] = __builtin_nontemporal_load(in + i);
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if constexpr (BF) {
-      const uint32_t word = w[i / 8][(i % 8) / 2];
+      const uint32_t word = w4[i / 8][(i % 8) / 2];
       x[i] = (i & 1) ? bf16_hi(word) : bf16_lo(word);
     } else {
-      x[i] = __uint_as_float(w[i / 4][i % 4]);
+      x[i] = __uint_as_float(w4[i / 4][i % 4]);
     }
   }
-  const float scale = is_v ? a.v_scale[0] : a.k_scale[0];
-  const u32x4 out = quantize16_e4m3(x, scale);
+  const u32x4 out = quantize16_e4m3(x, scale_rcp(is_v ? a.v_scale[0] : a.k_scale[0]));
   u32x4* pool = is_v ? a.v_cache : a.k_cache;
   pool[dst] = out;
 }
 
 hipError_t launch_kv_write_fp8(const KvWriteFp8Args& a, DType src, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(a.num_tokens) * 2 * a.row_chunks;
-  if (items == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  if (a.num_tokens == 0 || a.row_chunks == 0) return hipSuccess;
+  const int64_t waves = static_cast<int64_t>(a.num_tokens) * ((2LL * a.row_chunks + 63) / 64);
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (src == DType::BF16)
     hipLaunchKernelGGL(kv_write_fp8_kernel<true>, grid, dim3(256), 0, stream, a);
   else

@@ -568,7 +568,7 @@ def main(argv=None):
                "history_write": {"tokens": fw_tokens, "kernel_avg_us": round(fw_ms * 1e3, 1),
                                  "gbs": round(fw_bytes / (fw_ms * 1e-3) / 1e9, 1),
                                  "kernel": "kv_write_fp8_kernel<bf16> (paged_kv_write_fp8)",
-                                 "bound": "fp32 IEEE divisions of the quantiser (16 per 16-byte chunk of codes)"},
+                                 "bound": "vector arithmetic of the quantiser (16 correctly rounded divisions per 16-byte chunk of codes)"},
                "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(fgbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(FP8_TRAFFIC_FILE, DECODE_SOURCES),
