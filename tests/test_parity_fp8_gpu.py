@@ -2,7 +2,8 @@
 
 The write is compared bit for bit on whole pools: random rows, quotients a
 few ulps either side of every rounding midpoint, saturating magnitudes, NaN,
-skipped slots, and every bf16 bit pattern at five scales.  Decode reads a pool the GPU wrote itself and is compared with
+skipped slots, and every bf16 bit pattern at seven scales (two outside the
+range where the quantiser uses its split division).  Decode reads a pool the GPU wrote itself and is compared with
 the oracle's attention over the pool the oracle wrote (the two pools are
 first checked identical): single pass, split with the window-aware merge,
 sliding window, four group / block-size shapes, and the FP8 Llama-3-8B decode
@@ -83,7 +84,7 @@ def test_kv_write_fp8_bit_exact(dtype):
     np.testing.assert_array_equal(dvc.cpu().numpy(), ovc)
 
 
-@pytest.mark.parametrize("scale", [6 / 448, 0.37, 1.0, 3e-3, 1e4])
+@pytest.mark.parametrize("scale", [6 / 448, 0.37, 1.0, 3e-3, 1e4, 1e-12, 1e12])
 def test_kv_write_fp8_every_bf16_value(scale):
     # every bf16 bit pattern (NaNs, infinities, subnormals, both zeros) as K and
     # as V, in 512 tokens of one 128-dim head: whole pools bit-exact
