@@ -7,9 +7,9 @@
 // section 3.1 describe: tiles of Q, K and V are staged on chip, softmax and
 // both matrix products are fused, and only the result goes back to HBM.
 //
-// prefill_mfma_kernel (bf16, head_dim 128): a workgroup owns PM query rows
-// (16 per wave, NR waves stacked) of NW query heads that share one KV head, so
-// every K/V tile it stages serves NW * PM query rows.  K/V tiles of 64 keys are
+// prefill_mfma_kernel (bf16, head_dim 128): a workgroup of four waves owns PM
+// query rows (32 per wave, NR = 4 / NW waves stacked) of NW query heads that
+// share one KV head, so every K/V tile it stages serves NW * PM query rows.  K/V tiles of 64 keys are
 // double-buffered in LDS by LDS-DMA (global_load_lds, no VGPR round trip), row
 // major with XOR-swizzled 16-byte chunks.  S^T = K Q^T and O^T += V^T P^T are
 // both v_mfma_f32_16x16x32_bf16: the S^T accumulator layout (4 consecutive
