@@ -48,6 +48,37 @@ def oracle_decode(case, write=True):
     return out, lse, kc, vc
 
 
+@pytest.mark.parametrize("ps", [0, 256, 512])
+def test_decode_growing_scores_rescale_every_tile(ps):
+    # every key at position p is slope * p along one direction u, every query
+    # lies along u: a sequence's scores grow by about 0.1 nats per position, so
+    # the running max and O are rescaled at nearly every 16-key tile, and the
+    # partitions' lse values differ by hundreds (the reduce's weights span the
+    # whole fp32 exponent range)
+    case = wl.make_case(2, batch=6, ctx_min=300, ctx_max=2048, max_blocks_per_seq=128)
+    rng = np.random.default_rng(6)
+    sp = case.spec
+    bs, d = sp.block_size, sp.head_dim
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    kc = wl.bf16_bits_to_f32(case.k_cache).astype(np.float64)
+    for b in range(sp.batch):
+        for p in range(int(case.context_lens[b]) - 1):
+            blk = int(case.block_tables[b, p // bs])
+            kc[blk, :, p % bs, :] = 0.3 * p * u + 0.01 * rng.standard_normal((sp.num_kv_heads, d))
+    case.k_cache = wl.f32_to_bf16_bits(np.nan_to_num(kc).astype(np.float32))
+    case.k_cache[np.isnan(kc)] = wl.BF16_NAN                      # unused slots stay NaN
+    last = (case.context_lens.astype(np.int64) - 1).astype(np.float64)
+    case.k_new = wl.f32_to_bf16_bits((0.3 * last[:, None, None] * u[None, None, :]).astype(np.float32)
+                                     + np.zeros(case.k_new.shape, np.float32))
+    case.q = wl.f32_to_bf16_bits((4.0 * u[None, None, :] + 0.01 * rng.standard_normal(case.q.shape))
+                                 .astype(np.float32))
+    out, lse, _, _, _ = run_decode(case, ps)
+    ref_out, ref_lse, _, _ = oracle_decode(case)
+    assert ref_lse.min() > 25.0
+    assert_parity(out, lse, ref_out, ref_lse, sp.dtype, f"growing ps={ps}")
+
+
 # ---------------------------------------------------------------------------
 # cache write: the whole pool bit-exact
 # ---------------------------------------------------------------------------

@@ -50,6 +50,33 @@ def test_prefill_matches_oracle(name):
     assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, name)
 
 
+def _growing_scores(case, rng, slope=0.3, q_len=4.0):
+    """Rewrite q and k so that every query's scores grow along the keys: keys
+    are slope * position along one unit direction u (plus a little noise),
+    queries q_len * u.  Each 64-key tile then raises a row's max by about
+    0.1 nats per key, past the lazy-rescale slack, so the running max and O are
+    rescaled at nearly every tile."""
+    d = case.spec.head_dim
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    cu = case.cu_seqlens.astype(np.int64)
+    pos = np.concatenate([np.arange(cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]).astype(np.float64)
+    k = slope * pos[:, None, None] * u[None, None, :] + 0.01 * rng.standard_normal(case.k.shape)
+    q = q_len * u[None, None, :] + 0.01 * rng.standard_normal(case.q.shape)
+    case.k = wl.f32_to_bf16_bits(k.astype(np.float32))
+    case.q = wl.f32_to_bf16_bits(q.astype(np.float32))
+    return case
+
+
+@pytest.mark.parametrize("lens", [(300, 700, 1030), (64, 65, 129)])
+def test_prefill_growing_scores_rescale_every_tile(lens):
+    case = _growing_scores(wl.make_case(3, num_seqs=len(lens), lens_fixed=lens), np.random.default_rng(5))
+    out, lse = run_prefill(case)
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype)
+    assert ref_lse.max() > 0.09 * (max(lens) - 1)   # the scores really grow along the keys
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, f"growing {lens}")
+
+
 @pytest.mark.parametrize("name", ["ragged_small", "g8"])
 def test_prefill_vector_kernel_matches_oracle(name):
     case = wl.make_case(3, **PREFILL_CASES[name])
