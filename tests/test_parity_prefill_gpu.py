@@ -77,6 +77,22 @@ def test_prefill_growing_scores_rescale_every_tile(lens):
     assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, f"growing {lens}")
 
 
+@pytest.mark.parametrize("window", [1, 40, 100, 257])
+def test_prefill_growing_scores_under_window(window):
+    # the same growing scores under a sliding window: a row's first visible key
+    # can lie in a later tile than the workgroup's first, so its running max
+    # goes from -inf to finite mid-loop and then keeps growing
+    lens = (300, 700, 1030)
+    case = _growing_scores(wl.make_case(3, num_seqs=len(lens), lens_fixed=lens), np.random.default_rng(7))
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    out, lse = ops.varlen_causal_prefill(q, k, v, to_dev(case.cu_seqlens), case.max_seqlen, case.scale, window=window)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, case.spec.dtype,
+                                      window=window)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype,
+                  f"growing, window {window}")
+
+
 @pytest.mark.parametrize("name", ["ragged_small", "g8"])
 def test_prefill_vector_kernel_matches_oracle(name):
     case = wl.make_case(3, **PREFILL_CASES[name])
