@@ -54,6 +54,49 @@ def oracle_of(case, heads=None):
                                 case.scale, case.spec.dtype, heads=heads)
 
 
+def _growing_paged(case, rng, slope=0.3, q_len=4.0):
+    """Keys at cached position p (prefix and chunk alike) become slope * p along
+    one direction u, queries q_len * u: scores grow along the keys, so the
+    running max and O are rescaled at nearly every tile."""
+    sp = case.spec
+    bs, d = sp.block_size, sp.head_dim
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    kc = wl.bf16_bits_to_f32(case.k_cache).astype(np.float64) if sp.dtype == wl.BF16 \
+        else case.k_cache.astype(np.float64)
+    knew = np.zeros(case.k_new.shape)
+    lq = np.diff(case.cu_seqlens_q.astype(np.int64))
+    for s in range(len(lq)):
+        ctx = int(case.context_lens[s])
+        pre = ctx - int(lq[s])
+        for p in range(pre):
+            kc[int(case.block_tables[s, p // bs]), :, p % bs, :] = slope * p * u + 0.01 * rng.standard_normal((sp.num_kv_heads, d))
+        a = int(case.cu_seqlens_q[s])
+        for i in range(int(lq[s])):
+            knew[a + i] = slope * (pre + i) * u + 0.01 * rng.standard_normal((sp.num_kv_heads, d))
+    q = q_len * u[None, None, :] + 0.01 * rng.standard_normal(case.q.shape)
+    nan = np.isnan(kc)
+    if sp.dtype == wl.BF16:
+        case.k_cache = wl.f32_to_bf16_bits(np.nan_to_num(kc).astype(np.float32))
+        case.k_cache[nan] = wl.BF16_NAN
+        case.k_new = wl.f32_to_bf16_bits(knew.astype(np.float32))
+        case.q = wl.f32_to_bf16_bits(q.astype(np.float32))
+    else:
+        case.k_cache = kc.astype(np.float32)
+        case.k_new = knew.astype(np.float32)
+        case.q = q.astype(np.float32)
+    return case
+
+
+@pytest.mark.parametrize("name", ["mixed_g4_bs16", "g8_bs32", "g1_bs8", "g2_bs64"])
+def test_paged_prefill_growing_scores(name):
+    case = _growing_paged(wl.make_case(6, **CASES[name]), np.random.default_rng(8))
+    kc, vc = write_pool(case)
+    out, lse = run(case, kc, vc)
+    ref_out, ref_lse = oracle_of(case)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, f"growing {name}")
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_paged_prefill_matches_oracle(name):
     case = wl.make_case(6, **CASES[name])
