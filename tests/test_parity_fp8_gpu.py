@@ -164,6 +164,38 @@ def test_decode_fp8_matches_oracle(name):
             assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"{name} ps={ps} window={window}")
 
 
+@pytest.mark.parametrize("name", ["g4_bs16", "g2_bs16"])
+def test_decode_fp8_growing_scores(name):
+    # every row written at position p is slope * p along one direction u and
+    # every query lies along u, so the scores grow along the positions (the
+    # E4M3 codes keep them monotone): the running max and O are rescaled at
+    # nearly every tile with the K scale folded into the softmax scale, and the
+    # split partitions carry lse values far apart
+    case = wl.make_case(8, **SHAPES[name])
+    rng = np.random.default_rng(9)
+    d = case.spec.head_dim
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    pos = np.concatenate([np.arange(int(c)) for c in case.context_lens]).astype(np.float64)
+    assert pos.size == case.k_new.shape[0]   # rows in (sequence, position) order
+    k = 0.3 * pos[:, None, None] * u[None, None, :] + 0.01 * rng.standard_normal(case.k_new.shape)
+    case.k_new = wl.f32_to_bf16_bits(k.astype(np.float32))
+    case.q = wl.f32_to_bf16_bits((4.0 * u[None, None, :] + 0.01 * rng.standard_normal(case.q.shape))
+                                 .astype(np.float32))
+    case.k_scale = float(np.float32(0.5))   # keeps 0.3 * p * u inside the E4M3 range
+    bs = case.spec.block_size
+    kc, vc, ks, vs = write_fp8_gpu(case)
+    okc, ovc = write_fp8_oracle(case)
+    np.testing.assert_array_equal(kc.cpu().numpy(), okc)
+    ref_out, ref_lse = oracle.decode(case.q, okc, ovc, case.block_tables, case.context_lens, bs, case.scale,
+                                     case.spec.dtype, kv_dtype=oracle.E4M3, k_scale=case.k_scale,
+                                     v_scale=case.v_scale)
+    assert ref_lse.max() > 40.0
+    for ps in (0, bs * 4):
+        out, lse = decode_fp8_gpu(case, kc, vc, ks, vs, ps, 0)
+        assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"growing {name} ps={ps}")
+
+
 def test_decode_fp8_scales_are_read_from_device():
     # changing only the device scalars changes the result as the oracle says
     # (scales near the written ones keep outputs O(1), where the bf16 bar applies)
