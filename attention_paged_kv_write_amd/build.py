@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -36,6 +37,22 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def source_digest() -> str:
+    """First 16 hex digits of a SHA-256 over every HIP source and header
+    (csrc/*.hip, csrc/*.h, include/*.h: name, then bytes, in name order).  The
+    library carries the digest of the sources it was built from (pa_build_id),
+    so a caller can tell whether a built .so matches the tree beside it."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h"))]
+    files += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    for path in sorted(files, key=lambda p: os.path.relpath(p, ROOT)):
+        h.update(os.path.relpath(path, ROOT).encode())
+        h.update(b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def _compile(src, verbose=False, extra=()):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
@@ -53,6 +70,7 @@ def build(jobs: int = 8, verbose: bool = False, extra=()) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    extra = (*extra, f'-DPA_BUILD_ID="{source_digest()}"')
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         results = list(ex.map(lambda s: _compile(s, verbose, extra), srcs))
     for obj, warn in results:

@@ -132,6 +132,11 @@ extern "C" {
 
 int pa_abi_version(void) { return 1; }
 
+#ifndef PA_BUILD_ID
+#define PA_BUILD_ID "unknown"
+#endif
+const char* pa_build_id(void) { return PA_BUILD_ID; }
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 int pa_set_option(int option, int value) {

@@ -10,7 +10,6 @@ fails to load, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -22,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 PA_F32, PA_BF16 = 0, 1
 PA_OPT_FORCE_VECTOR_PATH = 1
 EXPORTED_SYMBOLS = (
-    "pa_abi_version", "pa_last_error", "pa_set_option", "paged_kv_write",
+    "pa_abi_version", "pa_build_id", "pa_last_error", "pa_set_option", "paged_kv_write",
     "paged_attention_decode", "paged_attention_reduce", "varlen_causal_prefill",
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
@@ -53,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.pa_abi_version.restype = i32
     lib.pa_abi_version.argtypes = []
+    lib.pa_build_id.restype = ctypes.c_char_p
+    lib.pa_build_id.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_set_option.restype = i32
@@ -104,6 +105,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i32, i32, i32, i32, f32, i32, i32, vp]
     _lib = lib
     return lib
+
+
+def build_id() -> str:
+    """Source digest the loaded library was built from (pa_build_id)."""
+    return load_library().pa_build_id().decode()
+
+
+def check_build_id() -> str:
+    """Raise unless the loaded library was built from the sources in this tree."""
+    from .build import source_digest
+    want, got = source_digest(), build_id()
+    if got != want:
+        raise RuntimeError(f"{LIB_PATH} was built from sources {got}, the tree holds {want}: rebuild it "
+                           "(python -m attention_paged_kv_write_amd.build)")
+    return got
 
 
 def _check(rc: int) -> None:
@@ -229,7 +245,7 @@ def num_partitions(max_context_len: int, partition_size: int) -> int:
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor,
-                           max_context_len: int, scale: Optional[float] = None,
+                           max_context_len: int, scale: float,
                            partition_size: int = 0, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None,
                            part_out: Optional[torch.Tensor] = None,
@@ -252,8 +268,6 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         raise ValueError("paged_attention_decode: inconsistent q / cache shapes or dtypes")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("paged_attention_decode: block_tables / context_lens shape")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     pq = _dev(q, "q", ndim=3)
     pkc = _dev(k_cache, "k_cache", ndim=4)
     pvc = _dev(v_cache, "v_cache", ndim=4)
@@ -327,6 +341,8 @@ def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
         out = torch.empty((B, Hq, d), dtype=out_dtype, device=part_out.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=part_out.device)
+    if out.shape != (B, Hq, d) or lse.shape != (B, Hq):
+        raise ValueError("paged_attention_reduce: out must be [B, H_q, d] and lse [B, H_q]")
     dt = _dtype_code(out)
     _check(lib.paged_attention_reduce_window(_dev(out, "out", ndim=3), _dev(lse, "lse", torch.float32, 2),
                                              _dev(part_out, "part_out", torch.float32, 4),
@@ -339,7 +355,7 @@ def paged_attention_reduce(part_out: torch.Tensor, part_lse: torch.Tensor,
 
 def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           cu_seqlens: torch.Tensor, max_seqlen: int,
-                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                          scale: float, out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None,
                           window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal attention over sequences packed by cu_seqlens -> (out [T,H_q,d], lse [T,H_q]).
@@ -352,12 +368,12 @@ def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("varlen_causal_prefill: inconsistent q/k/v")
     if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
         raise ValueError("varlen_causal_prefill: cu_seqlens must be [num_seqs + 1]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or lse.shape != (T, Hq):
+        raise ValueError("varlen_causal_prefill: out must be [T, H_q, d] and lse [T, H_q]")
     _check(lib.varlen_causal_prefill_window(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
                                             _dev(q, "q", ndim=3), _dev(k, "k", ndim=3), _dev(v, "v", ndim=3),
                                             _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
@@ -368,7 +384,7 @@ def varlen_causal_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor, context_lens: torch.Tensor,
-                  max_seqlen_q: int, max_context_len: int, scale: Optional[float] = None,
+                  max_seqlen_q: int, max_context_len: int, scale: float,
                   out: Optional[torch.Tensor] = None,
                   lse: Optional[torch.Tensor] = None, window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """A chunk of query rows per sequence (the last rows of its cache) against its
@@ -383,12 +399,12 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if cu_seqlens_q.dim() != 1 or S < 0 or block_tables.dim() != 2 or block_tables.shape[0] != S \
             or context_lens.shape != (S,):
         raise ValueError("paged_prefill: cu_seqlens_q / block_tables / context_lens shape")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or lse.shape != (T, Hq):
+        raise ValueError("paged_prefill: out must be [T_q, H_q, d] and lse [T_q, H_q]")
     _check(lib.paged_prefill_window(_dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2),
                              _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
                              _dev(v_cache, "v_cache", ndim=4),

@@ -110,6 +110,7 @@ def main(argv=None):
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     ops.load_library()
+    build_id = ops.check_build_id()   # the .so that runs is the one built from these sources
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -638,6 +639,7 @@ def main(argv=None):
         "prefill": prefill,
         "window": window,
         "fp8": fp8,
+        "library_build_id": build_id,
     }
     print(json.dumps(line), flush=True)
 

@@ -78,6 +78,12 @@ enum {
 /* Version of this ABI (bumped on any signature or semantic change). */
 int pa_abi_version(void);
 
+/* Identity of the sources this library was built from: the first 16 hex digits
+ * of a SHA-256 over the library's HIP sources and headers (file name, then
+ * bytes, in name order), baked in at build time; "unknown" if the build did
+ * not supply it.  The string is static; the caller must not free it. */
+const char* pa_build_id(void);
+
 /* Process-wide options.  PA_OPT_FORCE_VECTOR_PATH (value 0/1): run decode and
  * prefill on their vector-ALU kernels even where an MFMA kernel exists (both
  * compute the same result; used to cross-check one kernel against the other).

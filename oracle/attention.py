@@ -38,8 +38,10 @@ Readings of points the pages leave open:
   * keys before the window take no part in any sum, so their blocks are
     never fetched: their table entries may name freed blocks (any value).
 
-Every function here has a pin in tests/test_oracle_pins.py (nothing is left
-parity-unpinned).
+Every function here is pinned by tests/test_oracle_pins.py (closed forms,
+torch SDPA, invariants, brute force), and tests/test_oracle_mutants.py plants
+plausible slips in them and checks that a pin catches each: nothing is left
+parity-unpinned.
 """
 from __future__ import annotations
 
@@ -158,22 +160,6 @@ def kv_rows(rows, dtype, kv_dtype, scale):
     if kv_dtype is None:
         return upcast(rows, dtype)
     return upcast(rows, kv_dtype) * float(np.float32(scale))
-
-
-def decode_one(q, k_cache, v_cache, block_tables, context_lens, block_size,
-               scale, dtype, b, h, positions=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
-    """Output and lse of query head h of sequence b (optionally a position range)."""
-    Hq = q.shape[1]
-    Hkv = k_cache.shape[1]
-    ctx = int(context_lens[b])
-    g = group_of(h, Hq, Hkv)
-    # gather from the KV head's slice of the pool only (a view, same bytes)
-    K = kv_rows(gather(k_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype, kv_dtype, k_scale)[:, 0, :]
-    V = kv_rows(gather(v_cache[:, g:g + 1], block_tables[b], ctx, block_size), dtype, kv_dtype, v_scale)[:, 0, :]
-    if positions is not None:
-        lo, hi = positions
-        K, V = K[lo:hi], V[lo:hi]
-    return attend(upcast(q[b, h], dtype), K, V, scale)
 
 
 def window_start(pos, window):

@@ -37,11 +37,6 @@ def quantize(x, dtype, scale) -> np.ndarray:
     return e4m3_encode(q)
 
 
-def dequantize(codes, scale) -> np.ndarray:
-    """code value times the fp32 scale, in float64 (exact)."""
-    return e4m3_value(codes) * float(np.float32(scale))
-
-
 def kv_write_fp8(k_cache, v_cache, k, v, slot_mapping, block_size, dtype, k_scale, v_scale):
     """The cache write of ``attention.kv_write`` into E4M3 pools: token t with
     slot s >= 0 stores quantize(k[t]) and quantize(v[t]) at block s // bs,

@@ -47,6 +47,13 @@ def test_abi_version(lib):
     assert lib.pa_abi_version() == 1
 
 
+def test_build_id_matches_sources(lib):
+    # the library in the tree was built from the sources beside it
+    from attention_paged_kv_write_amd import build
+    assert ops.build_id() == build.source_digest()
+    assert ops.check_build_id() == build.source_digest()
+
+
 def _decode(lib, **kw):
     a = dict(B=2, Hq=8, Hkv=2, d=128, bs=16, mbps=4, NB=10, psize=0, maxctx=64, scale=0.1, dt=1)
     a.update(kw)

@@ -127,7 +127,49 @@ def _reduce_window_skips_first_partition(part_out, part_lse, context_lens, parti
     return oa.__dict__["_orig_reduce"](part_out, part_lse, context_lens, partition_size, window)
 
 
+def _upcast_bf16_as_integers(x, dtype):
+    # bf16 bit patterns widened as if they were integer values
+    if dtype == oa.BF16:
+        return np.asarray(x).astype(np.float64)
+    return oa.__dict__["_orig_upcast"](x, dtype)
+
+
+def _decode_drops_newest(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, dtype,
+                         return_probs=False, window=0, kv_dtype=None, k_scale=1.0, v_scale=1.0):
+    # the query attends to positions 0..ctx-2 (the token just written is left out)
+    lens = np.maximum(np.asarray(context_lens) - 1, 1)
+    return oa.__dict__["_orig_decode"](q, k_cache, v_cache, block_tables, lens, block_size, scale, dtype,
+                                       return_probs, window, kv_dtype, k_scale, v_scale)
+
+
+def _partitions_start_one_late(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, dtype,
+                               partition_size, max_partitions=None, window=0, kv_dtype=None,
+                               k_scale=1.0, v_scale=1.0):
+    # every partition but the first starts one position late (its first key is lost)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    P = max_partitions or oa.num_partitions(int(np.max(context_lens)), partition_size)
+    po = np.zeros((B, Hq, P, d))
+    pl = np.full((B, Hq, P), -math.inf)
+    for b in range(B):
+        ctx = int(context_lens[b])
+        K = oa.upcast(oa.gather(k_cache, block_tables[b], ctx, block_size), dtype)
+        V = oa.upcast(oa.gather(v_cache, block_tables[b], ctx, block_size), dtype)
+        for i in range(P):
+            lo, hi = i * partition_size + (1 if i else 0), min((i + 1) * partition_size, ctx)
+            if lo >= hi:
+                continue
+            for h in range(Hq):
+                g = oa.group_of(h, Hq, Hkv)
+                o, l, _ = oa.attend(oa.upcast(q[b, h], dtype), K[lo:hi, g], V[lo:hi, g], scale)
+                po[b, h, i], pl[b, h, i] = o, l
+    return po, pl
+
+
 MUTANTS = {
+    "bf16_widened_as_integers": [("upcast", _upcast_bf16_as_integers)],
+    "decode_drops_newest_position": [("decode", _decode_drops_newest)],
+    "partitions_start_one_late": [("decode_partitions", _partitions_start_one_late)],
     "group_map_h_mod_G": [("group_of", _group_mod)],
     "dropped_scale": [("attend", _attend_no_scale)],
     "lse_in_log2": [("attend", _attend_log2)],
@@ -156,6 +198,7 @@ PIN_CALLS = [
     lambda g: pins.test_paged_prefill_equals_masked_sdpa((7, 40, 100), (7, 13, 1), 16),
     lambda g: pins.test_window_decode_equals_masked_sdpa_and_split_merge(7),
     lambda g: pins.test_window_decode_equals_masked_sdpa_and_split_merge(40),
+    lambda g: pins.test_decode_bf16_upcast_exact(),
 ]
 
 
@@ -163,6 +206,8 @@ PIN_CALLS = [
 def test_pins_catch_planted_mistake(name, golden_dir, monkeypatch):
     monkeypatch.setitem(oa.__dict__, "_orig_attend", oa.attend)
     monkeypatch.setitem(oa.__dict__, "_orig_reduce", oa.reduce_partitions)
+    monkeypatch.setitem(oa.__dict__, "_orig_upcast", oa.upcast)
+    monkeypatch.setitem(oa.__dict__, "_orig_decode", oa.decode)
     for fn_name, repl in MUTANTS[name]:
         monkeypatch.setattr(oa, fn_name, repl)
         if hasattr(oracle, fn_name):

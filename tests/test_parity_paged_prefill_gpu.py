@@ -177,11 +177,9 @@ def test_context_shorter_than_chunk_leaves_rows_untouched():
 
 
 @pytest.mark.slow
-def test_full_chunked_prefill_workload_sampled_heads():
+def test_full_chunked_prefill_workload_every_output():
     case = wl.make_case(6)
     kc, vc = write_pool(case)
     out, lse = run(case, kc, vc)
-    heads = [0, 13, 31]
-    ref_out, ref_lse = oracle_of(case, heads=heads)
-    o, l = to_host_f64(out), to_host_f64(lse)
-    assert_parity(o[:, heads], l[:, heads], ref_out[:, heads], ref_lse[:, heads], case.spec.dtype, "workload 6")
+    ref_out, ref_lse = oracle_of(case)
+    assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, case.spec.dtype, "workload 6, every output")

@@ -184,12 +184,10 @@ def test_prefill_write_then_decode_cross_path():
 
 
 @pytest.mark.slow
-def test_prefill_full_size_sampled_heads():
+def test_prefill_full_size_every_output():
+    # workload 3 at full size (16 sequences, about 17k rows): every row of every head
     case = wl.make_case(3)
     out, lse = run_prefill(case)
     oh, lh = to_host_f64(out), to_host_f64(lse)
-    heads = [0, 13, 31]
-    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, wl.BF16,
-                                      heads=heads)
-    assert_parity(oh[:, heads], lh[:, heads], ref_out[:, heads], ref_lse[:, heads], wl.BF16, "full C3")
-    assert np.isfinite(oh).all() and np.isfinite(lh).all()
+    ref_out, ref_lse = oracle.prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, wl.BF16)
+    assert_parity(oh, lh, ref_out, ref_lse, wl.BF16, "workload 3, every (row, head)")

@@ -197,7 +197,7 @@ def test_window_paged_prefill(name, window):
 
 # ---------------------------------------------------------------------------
 # the sliding-window decode workload at full size (split as timed, and single
-# pass), oracle on a sample of sequences
+# pass), every (sequence, head) against the oracle
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def window_workload():
@@ -212,11 +212,6 @@ def test_window_decode_workload_full_size(window_workload, ps):
     case, kc, vc = window_workload
     W, bs = case.spec.window, case.spec.block_size
     out, lse = decode_window(case, ps, W)
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    lens = case.context_lens
-    # the shortest (whole history visible), the longest, and a spread between
-    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31, 47, 63})
-    for b in sample:
-        ro, rl = oracle.decode(case.q[b:b + 1], kc, vc, case.block_tables[b:b + 1], lens[b:b + 1], bs,
-                               case.scale, case.spec.dtype, window=W)
-        assert_parity(out[b:b + 1], lse[b:b + 1], ro, rl, case.spec.dtype, f"seq {b} ctx={int(lens[b])} ps={ps}")
+    ro, rl = oracle.decode(case.q, kc, vc, case.block_tables, case.context_lens, bs, case.scale,
+                           case.spec.dtype, window=W)
+    assert_parity(out, lse, ro, rl, case.spec.dtype, f"workload 7, every output, ps={ps}")
