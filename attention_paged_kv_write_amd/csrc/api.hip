@@ -40,16 +40,18 @@ bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
 int esize(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+// Partition dimension of a split decode's partials.
+int split_parts(int max_context_len, int partition_size) {
+  return max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+}
 
-// Validation, arguments and launch shared by the decode entry points: plain or
-// sliding window, bf16/f32 or E4M3 pools (kv8, with device-side scales), and
-// with or without the new token's K/V (k_new, v_new) appended by the kernel.
-int decode_call(const char* fn, void* out, float* lse, float* part_out, float* part_lse, const void* q,
-                const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
-                const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
-                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
-                int partition_size, int max_context_len, float scale, int window, pa_dtype dtype, bool kv8,
-                const float* k_scale, const float* v_scale, void* stream) {
+// Host-side checks of a decode call (everything but the output pointers);
+// PA_OK means the launch may proceed (num_seqs may still be 0: nothing to do).
+int decode_check(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                 int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                 int partition_size, int max_context_len, float scale, int window, pa_dtype dtype, bool kv8,
+                 const float* k_scale, const float* v_scale) {
   if (window < 0) return fail(PA_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
@@ -77,15 +79,32 @@ int decode_call(const char* fn, void* out, float* lse, float* part_out, float* p
       return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
   }
   if (!group_ok(G)) return fail(PA_ERR_UNSUPPORTED, "%s: GQA group size %d", fn, G);
+  if (partition_size > 0 && split_parts(max_context_len, partition_size) > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
   if (num_seqs == 0) return ok();
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: null input pointer", fn);
   if (kv8 && (!k_scale || !v_scale)) return fail(PA_ERR_INVALID_ARG, "%s: null k_scale/v_scale", fn);
+  return PA_OK;
+}
+
+// Validation, arguments and launch shared by the decode entry points: plain or
+// sliding window, bf16/f32 or E4M3 pools (kv8, with device-side scales), and
+// with or without the new token's K/V (k_new, v_new) appended by the kernel.
+int decode_call(const char* fn, void* out, float* lse, float* part_out, float* part_lse, const void* q,
+                const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                int partition_size, int max_context_len, float scale, int window, pa_dtype dtype, bool kv8,
+                const float* k_scale, const float* v_scale, void* stream) {
+  const int rc = decode_check(fn, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                              num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, partition_size,
+                              max_context_len, scale, window, dtype, kv8, k_scale, v_scale);
+  if (rc != PA_OK || num_seqs == 0) return rc;
   int num_parts = 1;
   if (partition_size > 0) {
     if (!part_out || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: null part_out/part_lse", fn);
-    num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
-    if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
+    num_parts = split_parts(max_context_len, partition_size);
   } else if (!out || !lse) {
     return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
   }
@@ -334,6 +353,50 @@ int paged_attention_reduce(void* out, float* lse, const float* part_out, const f
                            int partition_size, int max_partitions, pa_dtype dtype, void* stream) {
   return paged_attention_reduce_window(out, lse, part_out, part_lse, context_lens, num_seqs, num_q_heads,
                                        head_dim, partition_size, max_partitions, 0, dtype, stream);
+}
+
+int paged_kv_stream_read(uint32_t* checksums, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                         int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, int partition_size,
+                         int max_context_len, int mode, int depth, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_kv_stream_read";
+  if (!dtype_ok(dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      partition_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: non-positive size", fn);
+  if (max_context_len < 0) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len > max_blocks_per_seq * block_size", fn);
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be a multiple of block_size", fn);
+  if (mode != PA_STREAM_LDS_DMA && mode != PA_STREAM_REGISTERS)
+    return fail(PA_ERR_INVALID_ARG, "%s: unknown mode %d", fn, mode);
+  if (dtype != PA_BF16 || head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "%s: bf16 head_dim 128 only", fn);
+  if (!(block_size == 16 || block_size == 32 || block_size == 64))
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs > 65535", fn);
+  const int num_parts = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+  if (num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 partitions", fn);
+  if (num_seqs == 0) return ok();
+  if (!checksums || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  pa::DecodeArgs a = {};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_kv_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.num_partitions = num_parts;
+  a.max_context_len = max_context_len;
+  return launch_status(pa::launch_stream(a, checksums, depth, mode == PA_STREAM_LDS_DMA,
+                                         static_cast<hipStream_t>(stream)), fn);
 }
 
 int paged_attention_reduce_window(void* out, float* lse, const float* part_out, const float* part_lse,

@@ -140,6 +140,10 @@ hipError_t launch_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStrea
 // The vector-ALU kernels alone (also the path for shapes without an MFMA kernel).
 hipError_t launch_decode_generic(const DecodeArgs& a, DType dt, int head_dim, hipStream_t stream);
 hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
+// The paged stream probe (stream.hip): decode's work units and tiles, read and
+// folded into XOR checksums [B, H_kv, P]; LDS-DMA ring of `depth` slots, or
+// `depth` tiles of register loads at a time.
+hipError_t launch_stream(const DecodeArgs& a, uint32_t* sums, int depth, bool dma, hipStream_t stream);
 // Paged prefill: the same kernels with keys read through the block table.
 hipError_t launch_paged_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
 hipError_t launch_paged_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);

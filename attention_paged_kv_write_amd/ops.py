@@ -26,8 +26,9 @@ EXPORTED_SYMBOLS = (
     "paged_prefill", "paged_attention_decode_window", "varlen_causal_prefill_window",
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
     "paged_attention_decode_fp8", "rope_cos_sin_cache", "paged_kv_write_rope",
-    "paged_attention_decode_append", "paged_attention_decode_append_fp8",
+    "paged_attention_decode_append", "paged_attention_decode_append_fp8", "paged_kv_stream_read",
 )
+PA_STREAM_LDS_DMA, PA_STREAM_REGISTERS = 0, 1
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
 
 _lib: Optional[ctypes.CDLL] = None
@@ -103,6 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_prefill_window.restype = i32
     lib.paged_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.paged_kv_stream_read.restype = i32
+    lib.paged_kv_stream_read.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                         i32, vp]
     _lib = lib
     return lib
 
@@ -414,3 +418,30 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              S, T, int(max_seqlen_q), Hq, Hkv, d, bs, block_tables.shape[1], NB,
                              int(max_context_len), float(scale), int(window), dt, _stream(q)))
     return out, lse
+
+
+def paged_kv_stream_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, max_context_len: int, partition_size: int,
+                         mode: int = PA_STREAM_LDS_DMA, depth: int = 2,
+                         checksums: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement call: read every K/V row a split decode with this partition
+    size reads, in its work units and tiles, and return the XOR of their 32-bit
+    words per (sequence, KV head, partition) as int32 [B, H_kv, P] (bit patterns)."""
+    lib = load_library()
+    NB, Hkv, bs, d = k_cache.shape
+    B = context_lens.shape[0]
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or block_tables.dim() != 2 \
+            or block_tables.shape[0] != B:
+        raise ValueError("paged_kv_stream_read: inconsistent shapes")
+    P = num_partitions(max_context_len, partition_size)
+    if checksums is None:
+        checksums = torch.empty((B, Hkv, P), dtype=torch.int32, device=k_cache.device)
+    if checksums.shape != (B, Hkv, P):
+        raise ValueError("paged_kv_stream_read: checksums must be [B, H_kv, P]")
+    _check(lib.paged_kv_stream_read(_dev(checksums, "checksums", torch.int32, 3), _dev(k_cache, "k_cache", ndim=4),
+                                    _dev(v_cache, "v_cache", ndim=4),
+                                    _dev(block_tables, "block_tables", torch.int32, 2),
+                                    _dev(context_lens, "context_lens", torch.int32, 1), B, Hkv, d, bs,
+                                    block_tables.shape[1], NB, int(partition_size), int(max_context_len), int(mode),
+                                    int(depth), _dtype_code(k_cache), _stream(k_cache)))
+    return checksums

@@ -39,6 +39,7 @@ METRIC = "paged decode KV GB/s (% HBM peak); varlen prefill TFLOP/s; Llama-3-8B 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 DECODE_SOURCES = ("attention_paged_kv_write_amd/csrc/decode.hip",
+                  "attention_paged_kv_write_amd/csrc/units.h",
                   "attention_paged_kv_write_amd/csrc/common.h",
                   "attention_paged_kv_write_amd/csrc/kernels.h")
 PREFILL_SOURCES = ("attention_paged_kv_write_amd/csrc/prefill.hip",
@@ -50,6 +51,12 @@ FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_fp8_llama3_8b.
 PAGED_PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_paged_prefill_llama3_8b.txt")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_window_llama3_8b.txt")
 ROPE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_kv_write_llama3_8b.txt")
+KV_WRITE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv_write_prompt_llama3_8b.txt")
+C4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama2_70b_prefix.txt")
+C5_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_long_context.txt")
+KV_WRITE_SOURCES = ("attention_paged_kv_write_amd/csrc/kv_write.hip",
+                    "attention_paged_kv_write_amd/csrc/common.h",
+                    "attention_paged_kv_write_amd/csrc/kernels.h")
 ROPE_SOURCES = ("attention_paged_kv_write_amd/csrc/rope.hip",
                 "attention_paged_kv_write_amd/csrc/common.h",
                 "attention_paged_kv_write_amd/csrc/kernels.h")
@@ -80,6 +87,105 @@ def measured_traffic(path, sources):
     return t.get("traffic_bytes_per_launch")
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return 1
+
+
+def host_note():
+    return f"host cpu_count={os.cpu_count()} affinity={len(os.sched_getaffinity(0))}"
+
+
+def prefill_cpu_baseline(pc, seconds):
+    """The fp64 oracle's varlen prefill on whole sequences of the same
+    workload, in order, until `seconds` have passed: TFLOP/s over the same
+    algorithmic FLOP count as the GPU figure."""
+    import oracle
+    lens = np.diff(pc.cu_seqlens).astype(np.int64)
+    t0 = time.perf_counter()
+    done, fl = 0, 0.0
+    while time.perf_counter() - t0 < seconds and done < len(lens):
+        oracle.prefill(pc.q, pc.k, pc.v, pc.cu_seqlens, pc.scale, pc.spec.dtype, seqs=[done])
+        fl += 4.0 * pc.spec.head_dim * pc.spec.num_q_heads * float(lens[done] * (lens[done] + 1) // 2)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle prefill of the first {done} of {len(lens)} sequences "
+                      f"({int(lens[:done].sum())} rows, all {pc.spec.num_q_heads} heads) in {dt:.2f} s; "
+                      f"BLAS threads {blas_threads()}, {host_note()}"}
+
+
+def decode_cpu_baseline(case, seconds, unique_bytes_per_kv_byte=1.0):
+    """The fp64 oracle's decode of whole sequences of the same workload, in
+    order (cycling), until `seconds` have passed: GB/s of KV processed."""
+    import oracle
+    spec = case.spec
+    B, Hkv, d = spec.batch, spec.num_kv_heads, spec.head_dim
+    t0 = time.perf_counter()
+    n, nbytes = 0, 0
+    while time.perf_counter() - t0 < seconds:
+        b = n % B
+        oracle.decode(case.q[b:b + 1], case.k_cache, case.v_cache, case.block_tables[b:b + 1],
+                      case.context_lens[b:b + 1], spec.block_size, case.scale, spec.dtype)
+        n += 1
+        nbytes += int(case.context_lens[b]) * Hkv * 2 * d * 2
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * unique_bytes_per_kv_byte / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle decode of {n} sequences in order ({nbytes / 1e6:.1f} MB of KV) "
+                      f"in {dt:.2f} s; BLAS threads {blas_threads()}, {host_note()}"}
+
+
+def timed_groups(torch, stream, fn, n_items, n_groups, group=10):
+    """Per-launch ms of fn(i) over n_groups groups of `group` back-to-back
+    launches (i rotating over n_items input copies), HIP events recorded on
+    the launch stream around each group."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_groups)]
+    torch.cuda.synchronize()
+    for gi in range(n_groups):
+        evs[gi][0].record(stream)
+        for k in range(group):
+            fn((gi * group + k) % n_items)
+        evs[gi][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / group for a, b in evs]
+
+
+def graph_ms(torch, stream, fn, n_items, reps):
+    """ms per fn(i) when the n_items calls are captured once in a HIP graph
+    and the graph is replayed `reps` times (no host launch cost); None if the
+    capture fails."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_items):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_items):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (reps * n_items)
+        del g
+        return ms
+    except Exception as e:  # pragma: no cover - depends on the runtime
+        log(f"graph capture failed: {e}")
+        return None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +197,8 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window figures")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache figures")
+    ap.add_argument("--no-c4", action="store_true", help="skip the Llama-2-70B prefix-sharing decode figures")
+    ap.add_argument("--no-c5", action="store_true", help="skip the long-context split-KV decode figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -223,6 +331,59 @@ def main(argv=None):
                 "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
                 "algorithmic_bytes_per_launch": kv_bytes}
     log(f"decode kernel avg {dec_avg_ms * 1e3:.1f} us -> {achieved_gbs:.0f} GB/s")
+
+    # Both steps again with their launches captured in a HIP graph (one capture
+    # holds one step per input copy), so the figure is GPU time, not Python.
+    graph_reps = max(1, args.steps // len(copies))
+    g2 = graph_ms(torch, stream, lambda i: step(copies[i]), len(copies), graph_reps)
+    g3 = graph_ms(torch, stream, lambda i: step_separate(copies[i]), len(copies), graph_reps)
+    log(f"graph-captured step: {g2 * 1e3 if g2 else float('nan'):.1f} us (two launches), "
+        f"{g3 * 1e3 if g3 else float('nan'):.1f} us (three launches)")
+
+    # The same decode kernel at other partition sizes (0 = one pass per
+    # (sequence, KV head) writing out/lse directly, no reduce needed).
+    variants = {}
+    for vps in sorted({0, 128, 256, 512} - {ps}):
+        vP = ops.num_partitions(maxctx, vps) if vps else 1
+        vbuf = [dict(po=torch.empty((B, Hq, vP, d), dtype=torch.float32, device=dev),
+                     pl=torch.empty((B, Hq, vP), dtype=torch.float32, device=dev)) if vps else None
+                for _ in copies]
+
+        def vdecode(i, vps=vps, vbuf=vbuf):
+            c = copies[i]
+            if vps:
+                ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], maxctx, case.scale, vps,
+                                           part_out=vbuf[i]["po"], part_lse=vbuf[i]["pl"])
+            else:
+                ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], maxctx, case.scale,
+                                           out=c["out"], lse=c["lse"])
+        for i in range(len(copies)):
+            vdecode(i)
+        vms = float(np.mean(timed_groups(torch, stream, vdecode, len(copies), n_groups)))
+        variants[str(vps)] = {"kernel_avg_us": round(vms * 1e3, 2),
+                              "gbs": round(kv_bytes / (vms * 1e-3) / 1e9, 1)}
+        del vbuf
+    roofline["partition_size_variants"] = variants
+    log("decode kernel by partition size: " +
+        ", ".join(f"{k}: {v['kernel_avg_us']} us" for k, v in variants.items()))
+
+    # Paged stream probe: the decode's work units and tiles read with no
+    # attention (paged_kv_stream_read), LDS-DMA rings of 2 (the decode
+    # kernel's), 3 and 4 slots, and register loads 4 tiles at a time.
+    sums = [torch.empty((B, Hkv, P), dtype=torch.int32, device=dev) for _ in copies]
+    probe = {}
+    for mode, depth, name in ((ops.PA_STREAM_LDS_DMA, 2, "lds_dma_ring_2"), (ops.PA_STREAM_LDS_DMA, 3, "lds_dma_ring_3"),
+                              (ops.PA_STREAM_LDS_DMA, 4, "lds_dma_ring_4"), (ops.PA_STREAM_REGISTERS, 4, "registers_4")):
+        def sread(i, mode=mode, depth=depth):
+            c = copies[i]
+            ops.paged_kv_stream_read(c["kc"], c["vc"], c["bt"], c["cl"], maxctx, ps, mode, depth, checksums=sums[i])
+        for i in range(len(copies)):
+            sread(i)
+        sms = float(np.mean(timed_groups(torch, stream, sread, len(copies), n_groups)))
+        probe[name] = {"kernel_avg_us": round(sms * 1e3, 2), "gbs": round(kv_bytes / (sms * 1e-3) / 1e9, 1)}
+    best_probe = max(v["gbs"] for v in probe.values())
+    log("paged stream probe: " + ", ".join(f"{k}: {v['gbs']} GB/s" for k, v in probe.items()))
+    del sums
     del copies
     torch.cuda.empty_cache()
 
@@ -247,9 +408,13 @@ def main(argv=None):
     cb.record(stream)
     torch.cuda.synchronize()
     read_gbs = nb * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
-    stream_ceiling = {"kind": "torch on 1 GiB: device copy (read + write bytes) and fp32 sum (read bytes)",
+    stream_ceiling = {"kind": "paged stream probe on the decode workload's own pools, tables and work units "
+                              "(paged_kv_stream_read, KV bytes per launch / launch time); torch on 1 GiB: device "
+                              "copy (read + write bytes) and fp32 sum (read bytes)",
+                      "paged_stream": probe,
                       "copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
-                      "frac_of_peak": round(max(copy_gbs, read_gbs) / HBM_PEAK_GBS, 4)}
+                      "frac_of_peak": round(max(copy_gbs, read_gbs, best_probe) / HBM_PEAK_GBS, 4),
+                      "decode_over_best_paged_stream": round(achieved_gbs / best_probe, 4)}
     log(f"device copy {copy_gbs:.0f} GB/s, sum {read_gbs:.0f} GB/s")
     del src, dst
     torch.cuda.empty_cache()
@@ -265,57 +430,58 @@ def main(argv=None):
         # q, k, v read once; out and lse written once
         T_, Hq_, Hkv_, d_ = pc.total_tokens, pc.spec.num_q_heads, pc.spec.num_kv_heads, pc.spec.head_dim
         io_bytes = T_ * (2 * Hq_ + 2 * Hkv_) * d_ * 2 + T_ * Hq_ * 4
-        pq, pk, pv, pcu = up(pc.q), up(pc.k), up(pc.v), up(pc.cu_seqlens)
-        pout = torch.empty_like(pq)
-        plse = torch.empty((pc.total_tokens, pc.spec.num_q_heads), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            ops.varlen_causal_prefill(pq, pk, pv, pcu, pc.max_seqlen, pc.scale, out=pout, lse=plse)
-        torch.cuda.synchronize()
-        pa_, pb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        pa_.record(stream)
-        for _ in range(args.prefill_iters):
-            ops.varlen_causal_prefill(pq, pk, pv, pcu, pc.max_seqlen, pc.scale, out=pout, lse=plse)
-        pb_.record(stream)
-        torch.cuda.synchronize()
-        pms = pa_.elapsed_time(pb_) / args.prefill_iters
+        # two copies of q, k, v (2 x 211 MB) alternate, so one launch's inputs
+        # are not in the 256 MB Infinity Cache from the launch before
+        pcu = up(pc.cu_seqlens)
+        pcopies = [dict(q=up(pc.q), k=up(pc.k), v=up(pc.v)) for _ in range(2)]
+        for c in pcopies:
+            c["out"] = torch.empty_like(c["q"])
+            c["lse"] = torch.empty((pc.total_tokens, pc.spec.num_q_heads), dtype=torch.float32, device=dev)
+        pq, pk, pv = pcopies[0]["q"], pcopies[0]["k"], pcopies[0]["v"]
+
+        def pfill(i):
+            c = pcopies[i]
+            ops.varlen_causal_prefill(c["q"], c["k"], c["v"], pcu, pc.max_seqlen, pc.scale, out=c["out"],
+                                      lse=c["lse"])
+        for i in range(3):
+            pfill(i % 2)
+        p_ms = timed_groups(torch, stream, pfill, 2, max(1, args.prefill_iters // 5), group=5)
+        pms = float(np.mean(p_ms))
         tflops = flops / (pms * 1e-3) / 1e12
-        # paged write-through of the prompt K/V
-        pool = torch.empty((pc.num_blocks, pc.spec.num_kv_heads, pc.spec.block_size, pc.spec.head_dim),
-                           dtype=torch.bfloat16, device=dev)
-        pool_v = torch.empty_like(pool)
+        # paged write-through of the prompt K/V: four copies of the source rows
+        # (4 x 70 MB) and two pools alternate; HIP events around groups of 10
+        # back-to-back writes
+        pools = [(torch.empty((pc.num_blocks, pc.spec.num_kv_heads, pc.spec.block_size, pc.spec.head_dim),
+                              dtype=torch.bfloat16, device=dev),
+                  torch.empty((pc.num_blocks, pc.spec.num_kv_heads, pc.spec.block_size, pc.spec.head_dim),
+                              dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+        pool, pool_v = pools[0]
+        wsrc = [(pcopies[0]["k"], pcopies[0]["v"]), (pcopies[1]["k"], pcopies[1]["v"]),
+                (up(pc.k), up(pc.v)), (up(pc.k), up(pc.v))]
         slots = up(pc.slot_mapping)
-        # three warm-up writes, then HIP events on the launch stream around
-        # 20 back-to-back writes
-        for _ in range(3):
-            ops.paged_kv_write(pk, pv, pool, pool_v, slots)
-        wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        wa.record(stream)
-        for _ in range(20):
-            ops.paged_kv_write(pk, pv, pool, pool_v, slots)
-        wb.record(stream)
-        torch.cuda.synchronize()
-        wms = wa.elapsed_time(wb) / 20
+
+        def pwrite(i):
+            ops.paged_kv_write(wsrc[i][0], wsrc[i][1], pools[i % 2][0], pools[i % 2][1], slots)
+        for i in range(4):
+            pwrite(i)
+        wms = float(np.mean(timed_groups(torch, stream, pwrite, 4, 2)))
         wbytes = 2 * 2 * pc.total_tokens * pc.spec.num_kv_heads * pc.spec.head_dim * 2  # read + write, K and V
         # RoPE fused into the prompt's cache write (row positions 0 .. L-1 of each
         # sequence, base 10000): q and k rotated in place, rotated k and v into
-        # the pool; on copies, since every call turns q and k again
+        # the pool; on two copies of q, k, v (every call turns q and k again)
         cu_h = pc.cu_seqlens.astype(np.int64)
         rpos = torch.from_numpy(np.concatenate([np.arange(cu_h[i + 1] - cu_h[i]) for i in range(len(cu_h) - 1)])
                                 .astype(np.int32)).to(dev)
         rtab = ops.rope_cos_sin_cache(pc.max_seqlen, d_, 10000.0)
-        rq, rk = pq.clone(), pk.clone()
         rope_bytes = (2 * T_ * Hq_ * d_ * 2 + 3 * T_ * Hkv_ * d_ * 2 + 2 * T_ * Hkv_ * d_ * 2
                       + T_ * d_ * 4 + T_ * 8)
-        for _ in range(3):
-            ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
-        torch.cuda.synchronize()
-        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ra.record(stream)
-        for _ in range(20):
-            ops.paged_kv_write_rope(rq, rk, pv, pool, pool_v, slots, rpos, rtab)
-        rb.record(stream)
-        torch.cuda.synchronize()
-        rms = ra.elapsed_time(rb) / 20
+
+        def rwrite(i):
+            c = pcopies[i]
+            ops.paged_kv_write_rope(c["q"], c["k"], c["v"], pools[i][0], pools[i][1], slots, rpos, rtab)
+        for i in range(2):
+            rwrite(i)
+        rms = float(np.mean(timed_groups(torch, stream, rwrite, 2, 2)))
         rgbs = rope_bytes / (rms * 1e-3) / 1e9
         rope_write = {"workload": pc.spec.name + " prompt rows", "rot_dim": d_, "base": 10000.0,
                       "kernel_avg_us": round(rms * 1e3, 1),
@@ -325,9 +491,11 @@ def main(argv=None):
                                    "kernel": "rope_kv_write_kernel<bf16> (paged_kv_write_rope)",
                                    "algorithmic_bytes_per_launch": rope_bytes}}
         log(f"fused rope + kv write {rms * 1e3:.1f} us -> {rgbs:.0f} GB/s")
-        del rq, rk
         prefill = {"workload": pc.spec.name, "total_tokens": pc.total_tokens,
                    "kernel_avg_us": round(pms * 1e3, 1), "tflops": round(tflops, 1),
+                   "kernel_p10_us": round(float(np.percentile(p_ms, 10)) * 1e3, 1),
+                   "kernel_p90_us": round(float(np.percentile(p_ms, 90)) * 1e3, 1),
+                   "input_copies": 2,
                    "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                                 "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                                 "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
@@ -336,10 +504,16 @@ def main(argv=None):
                                 "algorithmic_bytes_per_launch": io_bytes},
                    "tokens_per_s": round(pc.total_tokens / (pms * 1e-3), 1),
                    "kv_write": {"kernel_avg_us": round(wms * 1e3, 1),
-                                "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1)},
+                                "gbs": round(wbytes / (wms * 1e-3) / 1e9, 1),
+                                "traffic": measured_traffic(KV_WRITE_TRAFFIC_FILE, KV_WRITE_SOURCES),
+                                "algorithmic_bytes_per_launch": wbytes,
+                                "input_copies": "4 source copies, 2 pools"},
                    "rope_kv_write": rope_write}
         log(f"prefill {pms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; prompt kv write {wms * 1e3:.1f} us")
-        del pq, pk, pv, pout, pool, pool_v
+        if not args.no_cpu_baseline:
+            prefill["cpu_baseline"] = prefill_cpu_baseline(pc, args.cpu_seconds)
+            log(f"prefill cpu baseline {prefill['cpu_baseline']['value']} TFLOP/s")
+        del pq, pk, pv, pool, pool_v, pcopies, pools, wsrc
         torch.cuda.empty_cache()
 
         # chunked prefill against a cached prefix (workload 6): the chunk's K/V are
@@ -360,6 +534,7 @@ def main(argv=None):
         for _ in range(3):
             chunked()
         torch.cuda.synchronize()
+        pa_, pb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         pa_.record(stream)
         for _ in range(args.prefill_iters):
             chunked()
@@ -582,15 +757,83 @@ def main(argv=None):
         del fcopies
         torch.cuda.empty_cache()
 
+    # ---------------------------------------------- workloads 4 and 5 (decode)
+    def decode_workload(cfg, n_copies, traffic_file, kernel_name):
+        t0 = time.perf_counter()
+        xc = wl.make_case(cfg)
+        xs = xc.spec
+        log(f"workload {cfg} generated in {time.perf_counter() - t0:.1f}s: NB={xc.num_blocks} "
+            f"sum(ctx)={int(xc.context_lens.sum())}")
+        xB, xHq, xHkv, xd, xbs, xps = (xs.batch, xs.num_q_heads, xs.num_kv_heads, xs.head_dim, xs.block_size,
+                                       xs.partition_size)
+        xmax = xc.max_context_len
+        xP = ops.num_partitions(xmax, xps)
+        ctx64 = xc.context_lens.astype(np.int64)
+        logical = int(ctx64.sum()) * xHkv * 2 * xd * 2
+        if xs.share_group:
+            shared = xs.share_blocks * xbs
+            unique = (xB // xs.share_group * shared + int((ctx64 - shared).sum())) * xHkv * 2 * xd * 2
+        else:
+            unique = logical
+        bt, cl = up(xc.block_tables), up(xc.context_lens)
+        xcopies = []
+        for _ in range(n_copies):
+            xcopies.append(dict(q=up(xc.q), kc=up(xc.k_cache), vc=up(xc.v_cache),
+                                po=torch.empty((xB, xHq, xP, xd), dtype=torch.float32, device=dev),
+                                pl=torch.empty((xB, xHq, xP), dtype=torch.float32, device=dev),
+                                out=torch.empty((xB, xHq, xd), dtype=torch.bfloat16, device=dev),
+                                lse=torch.empty((xB, xHq), dtype=torch.float32, device=dev)))
+
+        def xdecode(i):
+            c = xcopies[i]
+            ops.paged_attention_decode(c["q"], c["kc"], c["vc"], bt, cl, xmax, xc.scale, xps,
+                                       part_out=c["po"], part_lse=c["pl"])
+
+        def xstep(i):
+            xdecode(i)
+            c = xcopies[i]
+            ops.paged_attention_reduce(c["po"], c["pl"], cl, xps, out=c["out"], lse=c["lse"])
+        for i in range(4):
+            xstep(i % n_copies)
+        ng = max(2, args.steps // 40)
+        dms = timed_groups(torch, stream, xdecode, n_copies, ng)
+        sms = timed_groups(torch, stream, xstep, n_copies, ng)
+        davg, savg = float(np.mean(dms)), float(np.mean(sms))
+        ugbs = unique / (davg * 1e-3) / 1e9
+        res = {"workload": xs.name, "batch": xB, "num_q_heads": xHq, "num_kv_heads": xHkv, "block_size": xbs,
+               "partition_size": xps, "sum_context": int(ctx64.sum()), "num_blocks": xc.num_blocks,
+               "input_copies": n_copies, "kv_bytes_unique": unique, "kv_bytes_logical": logical,
+               "step_us": round(savg * 1e3, 2), "step_gbs_unique": round(unique / (savg * 1e-3) / 1e9, 1),
+               "logical_gbs": round(logical / (davg * 1e-3) / 1e9, 1),
+               "decode_tokens_per_s": round(xB / (savg * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(ugbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(ugbs / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic(traffic_file, DECODE_SOURCES),
+                            "kernel": kernel_name, "kernel_avg_us": round(davg * 1e3, 2),
+                            "kernel_p10_us": round(float(np.percentile(dms, 10)) * 1e3, 2),
+                            "kernel_p90_us": round(float(np.percentile(dms, 90)) * 1e3, 2),
+                            "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
+                            "algorithmic_bytes_per_launch": unique}}
+        log(f"workload {cfg}: decode kernel {davg * 1e3:.1f} us -> {ugbs:.0f} GB/s unique "
+            f"({logical / (davg * 1e-3) / 1e9:.0f} logical); step {savg * 1e3:.1f} us")
+        del xcopies, bt, cl
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = decode_cpu_baseline(xc, min(args.cpu_seconds, 5.0))
+            log(f"workload {cfg} cpu baseline {res['cpu_baseline']['value']} GB/s")
+        return res
+
+    # the pools of one copy (2.5-2.7 GB) exceed the Infinity Cache many times over
+    c4 = None if args.no_c4 else decode_workload(
+        4, 2, C4_TRAFFIC_FILE, "decode_mfma_kernel<G=8,BS=32,W=1> (paged_attention_decode)")
+    c5 = None if args.no_c5 else decode_workload(
+        5, 1, C5_TRAFFIC_FILE, "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode) + reduce_kernel")
+
     # ------------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover - threadpoolctl is optional
-            blas_threads = 1
+        n_blas = blas_threads()
         t0 = time.perf_counter()
         kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
         n_done = 0
@@ -602,13 +845,12 @@ def main(argv=None):
             n_done += 1
             bytes_done += int(case.context_lens[b]) * Hkv * 2 * d * 2
         cpu_s = time.perf_counter() - t0
-        cpu = {"value": round(bytes_done / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+        cpu = {"value": round(bytes_done / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(n_blas),
                "kind": "oracle",
                "sample": f"fp64 NumPy oracle on the same workload: paged write of the 64 new tokens, "
                          f"then decode of {n_done} sequences in order, cycling over the 64 "
                          f"({n_done / B:.1f} passes, {bytes_done / 1e6:.1f} MB of KV) in {cpu_s:.2f} s; "
-                         f"BLAS threads {blas_threads}, host cpu_count={os.cpu_count()} "
-                         f"affinity={len(os.sched_getaffinity(0))}"}
+                         f"BLAS threads {n_blas}, {host_note()}"}
         log(f"cpu baseline {cpu['value']} GB/s on {n_done} sequences")
 
     line = {
@@ -631,6 +873,8 @@ def main(argv=None):
                    "step": "paged_attention_decode_append (the 64 new tokens' cache write folded in) + "
                            "paged_attention_reduce",
                    "ms_per_step_three_launches": round(sep_ms, 5),
+                   "graph_ms_per_step": g2 and round(g2, 5),
+                   "graph_ms_per_step_three_launches": g3 and round(g3, 5),
                    "kv_bytes_per_step": kv_bytes},
         "roofline": roofline,
         "decode_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
@@ -639,6 +883,8 @@ def main(argv=None):
         "prefill": prefill,
         "window": window,
         "fp8": fp8,
+        "c4": c4,
+        "c5": c5,
         "library_build_id": build_id,
     }
     print(json.dumps(line), flush=True)

@@ -386,6 +386,36 @@ int paged_kv_write_rope(void* q, void* k, const void* v, void* k_cache, void* v_
                         int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
                         int block_size, int num_blocks, int max_positions, pa_dtype dtype, void* stream);
 
+/*
+ * paged_kv_stream_read - a measurement call, not a step of the method: the
+ * bandwidth ceiling of the split-KV decode's memory access pattern.
+ *
+ * It walks the work units paged_attention_decode walks with this
+ * partition_size (KV head g, sequence b, partition i; the same balanced order)
+ * and reads every K and V row of positions [i*partition_size,
+ * min((i+1)*partition_size, ctx)) through the block table, in the same
+ * 16-position tiles of one (block, KV head) slab, doing no attention.  So that
+ * every fetched byte is used and the result can be checked, it writes
+ *   checksums[b, g, i] = XOR of every 32-bit word of those K rows and V rows
+ *                        of KV head g (uint32 [num_seqs, num_kv_heads, P],
+ *                        P = ceil(max_context_len / partition_size));
+ * partitions past the end of a sequence are not written.
+ *   mode PA_STREAM_LDS_DMA:   tiles reach LDS by LDS-DMA (as in the decode
+ *                             kernel) through a ring of `depth` slots (2, 3 or
+ *                             4): depth - 1 tiles in flight per wave;
+ *   mode PA_STREAM_REGISTERS: 16-byte loads into registers, `depth` tiles (1,
+ *                             2 or 4) issued together.
+ * Other arguments as for paged_attention_decode.  Supported: PA_BF16, head_dim
+ * 128, block_size 16, 32 or 64.  Returns PA_ERR_UNSUPPORTED for an unsupported
+ * depth.
+ */
+enum { PA_STREAM_LDS_DMA = 0, PA_STREAM_REGISTERS = 1 };
+int paged_kv_stream_read(uint32_t* checksums, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                         int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                         int num_blocks, int partition_size, int max_context_len, int mode, int depth,
+                         pa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

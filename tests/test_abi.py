@@ -201,3 +201,16 @@ def test_append_validation(lib):
     assert lib.paged_attention_decode_append(*base(), -1, 1, None) == 1              # negative window
     assert lib.paged_attention_decode_append_fp8(*base(kn=None), p, p, 0, 1, None) == 1
     assert lib.paged_attention_decode_append_fp8(*base(), None, p, 0, 1, None) == 1  # null scale
+
+
+def test_stream_probe_validation(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.paged_kv_stream_read
+    # checksums, k, v, tables, lens, B, Hkv, d, bs, mbps, NB, psize, maxctx, mode, depth, dtype, stream
+    assert f(p, p, p, p, p, 2, 8, 128, 16, 4, 10, 24, 64, 0, 2, 1, None) == 1   # partition not a multiple
+    assert f(p, p, p, p, p, 2, 8, 128, 16, 4, 10, 64, 65, 0, 2, 1, None) == 1   # max_context_len too long
+    assert f(p, p, p, p, p, 2, 8, 128, 16, 4, 10, 64, 64, 7, 2, 1, None) == 1   # unknown mode
+    assert f(p, p, p, p, p, 2, 8, 128, 16, 4, 10, 64, 64, 0, 2, 0, None) == 2   # f32 pools
+    assert f(p, p, p, p, p, 2, 8, 64, 16, 4, 10, 64, 64, 0, 2, 1, None) == 2    # head_dim 64
+    assert f(None, None, None, None, None, 2, 8, 128, 16, 4, 10, 64, 64, 0, 2, 1, None) == 1
+    assert f(p, p, p, p, p, 0, 8, 128, 16, 4, 10, 64, 64, 0, 2, 1, None) == 0   # nothing to do
