@@ -297,50 +297,53 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   merge_and_store<BF, D, G>(a, b, g, part, sm_m, sm_l, sm_acc);
 }
 
-// Read one decode tile back from its LDS slot: the four lane-linear 16-byte K
-// reads and the eight transposed V reads, then wait for them.  Inline asm (only
-// in the device pass: its register constraints mean nothing to the host
-// compiler) so that the compiler, which cannot track LDS-DMA completions, adds
-// no wait of its own for the DMA loads in flight.
+// Read one decode tile back from its LDS ring slot: the four lane-linear
+// 16-byte K reads and the eight transposed V reads, then wait for them.  The
+// slot's byte offset OFF is an immediate of each read (no address arithmetic
+// per tile).  Inline asm (only in the device pass: its register constraints
+// mean nothing to the host compiler) so that the compiler, which cannot track
+// LDS-DMA completions, adds no wait of its own for the DMA loads in flight.
+template <int OFF>
 __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const uint32_t* k_addr,
-                                                     const uint32_t* v_addr, uint32_t off) {
+                                                     const uint32_t* v_addr) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %13\n\t"
-      "ds_read_b128 %2, %14\n\t"
-      "ds_read_b128 %3, %15\n\t"
-      "ds_read_b64_tr_b16 %4, %16\n\t"
-      "ds_read_b64_tr_b16 %5, %17\n\t"
-      "ds_read_b64_tr_b16 %6, %18\n\t"
-      "ds_read_b64_tr_b16 %7, %19\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\t"
-      "ds_read_b64_tr_b16 %9, %21\n\t"
-      "ds_read_b64_tr_b16 %10, %22\n\t"
-      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "ds_read_b128 %0, %12 offset:%24\n\t"
+      "ds_read_b128 %1, %13 offset:%24\n\t"
+      "ds_read_b128 %2, %14 offset:%24\n\t"
+      "ds_read_b128 %3, %15 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %10, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %23 offset:%24\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(kw[2]), "=&v"(kw[3]), "=&v"(vt[0]), "=&v"(vt[1]),
         "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]), "=&v"(vt[6]), "=&v"(vt[7])
-      : "v"(k_addr[0] + off), "v"(k_addr[1] + off), "v"(k_addr[2] + off), "v"(k_addr[3] + off),
-        "v"(v_addr[0] + off), "v"(v_addr[1] + off), "v"(v_addr[2] + off), "v"(v_addr[3] + off),
-        "v"(v_addr[4] + off), "v"(v_addr[5] + off), "v"(v_addr[6] + off), "v"(v_addr[7] + off)
+      : "v"(k_addr[0]), "v"(k_addr[1]), "v"(k_addr[2]), "v"(k_addr[3]), "v"(v_addr[0]), "v"(v_addr[1]),
+        "v"(v_addr[2]), "v"(v_addr[3]), "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7]),
+        "i"(OFF)
       : "memory");
 #endif
 }
 
 // FP8 tile, first step: this lane's 32 K codes and 32 V codes (two 16-byte
-// reads each) from its LDS ring slot, then wait for them.
+// reads each) from its LDS ring slot (byte offset OFF), then wait for them.
+template <int OFF>
 __device__ __forceinline__ void lds_read_fp8_tile(u32x4* k8, u32x4* v8, const uint32_t* k_addr,
-                                                  const uint32_t* v_addr, uint32_t off) {
+                                                  const uint32_t* v_addr) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k8[0]), "=&v"(k8[1]), "=&v"(v8[0]), "=&v"(v8[1])
-      : "v"(k_addr[0] + off), "v"(k_addr[1] + off), "v"(v_addr[0] + off), "v"(v_addr[1] + off)
+      : "v"(k_addr[0]), "v"(k_addr[1]), "v"(v_addr[0]), "v"(v_addr[1]), "i"(OFF)
       : "memory");
 #endif
 }
@@ -422,7 +425,7 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // 32(l%4) .. +31 of token l/4 to bf16 into a per-wave staging tile laid out
 // like the bf16 V tile, which the transposed reads then use unchanged.  The
 // K scale multiplies the softmax scale, the V scale the output.
-template <int G, int BS, int W, bool KV8>
+template <int G, int BS, int W, bool KV8, int NS>
 __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int RC = D * 2 / 16;   // 16-byte chunks per bf16 row (16)
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   // bf16 V staging tile
   constexpr int kSlotChunks = KV8 ? 256 : 512;
   constexpr int kSlotBytes = kSlotChunks * 16;
-  __shared__ __attribute__((aligned(16))) u32x4 ring[W][2][kSlotChunks];
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][kSlotChunks];
   __shared__ __attribute__((aligned(16))) u32x4 stage[KV8 ? W : 1][KV8 ? 256 : 1];
   __shared__ float sm_m[W][G];
   __shared__ float sm_l[W][G];
@@ -462,6 +465,14 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   // First round trip: context length, the group's queries, and the first
   // window of block ids (speculative: bounded by the table row, masked below).
   const int ctx_raw = a.context_lens[b];
+  // The softmax scale (times the K scale of an E4M3 pool) multiplies the raw
+  // scores inside the exponent's FMA and the tile max only (max(s) * c =
+  // max(s * c) for c > 0); a negative scale is folded into Q by an exact sign
+  // flip of its bf16 values, and a zero one becomes the smallest normal float
+  // so that masked scores stay -inf.
+  const float sl2_raw = KV8 ? a.scale_log2 * a.k_scale[0] : a.scale_log2;
+  const float sl2 = fmaxf(fabsf(sl2_raw), 1.17549435e-38f);
+  const uint32_t qsign = sl2_raw < 0.f ? 0x80008000u : 0u;
   bf16x8 qf[4];
   {
     const u32x4* qc = static_cast<const u32x4*>(a.q);
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (c16 < G) w = qc[row * RC + (KV8 ? 4 * j + c : 4 * c + j)];
+      if (c16 < G) w = qc[row * RC + (KV8 ? 4 * j + c : 4 * c + j)] ^ qsign;
       qf[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -547,9 +558,29 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
     for (int dn = 0; dn < 8; ++dn)
       v_addr[dn] = lds_addr(&stage[wave][0]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
   }
-  // E4M3 scales (device scalars): K folds into the softmax scale, V into the output
-  const float sl2 = KV8 ? a.scale_log2 * a.k_scale[0] : a.scale_log2;
+  // E4M3: the V scale multiplies the output
   const float vsc = KV8 ? a.v_scale[0] : 1.f;
+  // Per-lane byte offsets of the tile's LDS-DMA loads from the (wave-uniform)
+  // start of its rows: row 4c + j (K) / 4k + j (V) at its swizzled chunk;
+  // E4M3: row 8i + lane/8.  Opaque, so that each load is a scalar base plus
+  // this 32-bit offset rather than 64-bit address arithmetic per load.
+  uint32_t dma_off[8];
+  if constexpr (!KV8) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int tok = 4 * c + j;
+      dma_off[c] = static_cast<uint32_t>((tok * RC + (c16 ^ tok)) * 16);
+      dma_off[4 + c] = static_cast<uint32_t>((tok * RC + (c16 ^ (2 * (tok & 7)))) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tok = 8 * i + (lane >> 3);
+      dma_off[i] = static_cast<uint32_t>((tok * RC8 + ((lane & 7) ^ (tok >> 1))) * 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
 
   for (int w0 = 0; w0 < n_blocks; w0 += 64) {
     if (w0 > 0) ids = load_ids(w0);
@@ -567,50 +598,62 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       phys = ok ? phys : 0;
       lim = ok ? r.ctx : 0;
     };
-    // Issue the LDS-DMA loads of window tile n into a ring slot (K then V, both
-    // row-major with the XOR chunk swizzle).
-    auto fetch = [&](int n, int slot) {
+    // Issue the LDS-DMA loads of window tile n into ring slot SLOT (K then V,
+    // both row-major with the XOR chunk swizzle).
+    auto fetch = [&](int n, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
       int pos0, lim, phys;
       tile_span(n, pos0, lim, phys);
       if constexpr (KV8) {
-        // 16 rows x 8 chunks per tile and pool: two loads of 64 chunks each;
-        // physical chunk lane%8 of row 8i + lane/8 holds chunk (lane%8) ^ (row/2)
+        // 16 rows x 8 chunks per tile and pool: two loads of 64 chunks each
         const size_t base8 = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC8;
+        const char* kb = reinterpret_cast<const char*>(kc + base8);
+        const char* vb = reinterpret_cast<const char*>(vc + base8);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int tok = 8 * i + (lane >> 3);
-          const int q = (lane & 7) ^ (tok >> 1);
-          global_to_lds16<PA_DECODE_AUX>(kc + base8 + tok * RC8 + q, &ring[wave][slot][64 * i]);
-          global_to_lds16<PA_DECODE_AUX>(vc + base8 + tok * RC8 + q, &ring[wave][slot][128 + 64 * i]);
+          global_to_lds16<PA_DECODE_AUX>(kb + dma_off[i], &ring[wave][SLOT][64 * i]);
+          global_to_lds16<PA_DECODE_AUX>(vb + dma_off[i], &ring[wave][SLOT][128 + 64 * i]);
         }
         return;
       }
       const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC;
+      const char* kb = reinterpret_cast<const char*>(kc + base);
+      const char* vb = reinterpret_cast<const char*>(vc + base);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int tok = 4 * c + j;   // 16 lanes per 256-byte row
-        global_to_lds16<PA_DECODE_AUX>(kc + base + tok * RC + (c16 ^ tok), &ring[wave][slot][64 * c]);
-      }
+      for (int c = 0; c < 4; ++c) global_to_lds16<PA_DECODE_AUX>(kb + dma_off[c], &ring[wave][SLOT][64 * c]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int tok = 4 * k + j;
-        const u32x4* src = vc + base + tok * RC + (c16 ^ (2 * (tok & 7)));
-        global_to_lds16<PA_DECODE_AUX>(src, &ring[wave][slot][256 + 64 * k]);
-      }
+      for (int k = 0; k < 4; ++k) global_to_lds16<PA_DECODE_AUX>(vb + dma_off[4 + k], &ring[wave][SLOT][256 + 64 * k]);
     };
 
-    // Compute window tile n from its ring slot (its loads have landed).
-    auto process = [&](int n, int slot) {
+    // Compute window tile n from ring slot SLOT (its loads have landed).
+    auto process = [&](int n, auto slot_c) {
+      constexpr int OFF = decltype(slot_c)::value * kSlotBytes;
       int pos0, lim, phys;
       tile_span(n, pos0, lim, phys);
-      const uint32_t off = slot * kSlotBytes;
       u32x4 kw[4];
       u32x2 vt[8];
+      // Rows past the end of the sequence may hold anything (NaN), and a zero
+      // probability times NaN is still NaN: in the tile that holds the end,
+      // each lane zeroes the V rows it fetched that lie past it (in LDS,
+      // before the reads; LDS operations of a wave complete in order).
+      if (pos0 + 16 > lim) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        if constexpr (!KV8) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (pos0 + 4 * k + j >= lim) ring[wave][SLOT][256 + 64 * k + lane] = zero;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            if (pos0 + 8 * i + (lane >> 3) >= lim) ring[wave][SLOT][128 + 64 * i + lane] = zero;
+        }
+      }
       if constexpr (!KV8) {
-        lds_read_decode_tile(kw, vt, k_addr, v_addr, off);
+        lds_read_decode_tile<OFF>(kw, vt, k_addr, v_addr);
       } else {
         u32x4 k8[2], v8[2];
-        lds_read_fp8_tile(k8, v8, k8_addr, v8_addr, off);
+        lds_read_fp8_tile<OFF>(k8, v8, k8_addr, v8_addr);
         u32x4 vb[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) vb[u] = e4m3x8_to_bf16(v8[u >> 1][2 * (u & 1)], v8[u >> 1][2 * (u & 1) + 1]);
@@ -622,14 +665,23 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[c]), qf[c], st, 0, 0, 0);
-      // st[i]: score of token pos0 + 4j + i for column c16
+      // st[i]: raw score of token pos0 + 4j + i for column c16.  A tile wholly
+      // inside the visible range (the common case) takes no mask; the others
+      // set their invisible scores to -inf (a wave-uniform branch).
+      const bool full = pos0 >= r.lo && pos0 + 16 <= lim;
       float s[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = pos0 + 4 * j + i;
-        s[i] = (pos < lim && pos >= r.lo) ? st[i] * sl2 : kNegInf;
+      for (int i = 0; i < 4; ++i) s[i] = st[i];
+      if (!full) {
+        int d0 = pos0 + 4 * j;
+        asm volatile("" : "+v"(d0));   // keeps the compares out of full tiles
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = (d0 + i < lim && d0 + i >= r.lo) ? s[i] : kNegInf;
       }
-      const float mx = quarter_max(vmax3(vmax3(s[0], s[1], s[2]), s[3], s[3]));
+      // IEEE maximum (v_maximum3_f32): compiler-visible, so its reads of the
+      // matrix-core results are ordered by the compiler
+      auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+      const float mx = quarter_max(mx2(mx2(s[0], s[1]), mx2(s[2], s[3]))) * sl2;
       // lazy rescale: the running max moves (with l and O) only when some
       // column's tile max exceeds it by more than the slack
       if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
@@ -643,37 +695,33 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       const float ms = m == kNegInf ? 0.f : m;   // no visible token yet (bad block ids)
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(s[i] - ms);
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(s[i], sl2, -ms));   // masked: exp2(-inf) = 0
       l += (p[0] + p[1]) + (p[2] + p[3]);
       const short4v pb = __builtin_bit_cast(short4v, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-      // tokens past the end may hold anything (NaN): their V entries are
-      // zero-selected, since a zero probability times NaN is still NaN
-      const bool tail = pos0 + 16 > lim;
 #pragma unroll
-      for (int dn = 0; dn < 8; ++dn) {
-        short4v va = __builtin_bit_cast(short4v, vt[dn]);
-        if (tail) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) va[k] = (pos0 + 4 * j + k < lim) ? va[k] : short(0);
-        }
-        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[dn], 0, 0, 0);
-      }
+      for (int dn = 0; dn < 8; ++dn)
+        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, vt[dn]), pb, oacc[dn], 0,
+                                                              0, 0);
     };
-
-    // Two-slot ring: tile n+1's loads are issued before tile n is computed;
-    // the wait then lets exactly those 8 loads (4 for E4M3) stay in flight (none after the
-    // last tile, so no tile is fetched twice).  The compiler cannot count
-    // LDS-DMA completions, so the waits are explicit.
-    fetch(0, 0);
-    for (int n = 0; n < nt; ++n) {
-      const int slot = n & 1;
-      if (n + 1 < nt) {
-        fetch(n + 1, slot ^ 1);
-        wait_vmcnt<KV8 ? 4 : 8>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      process(n, slot);
+    // Ring of NS slots: tile n + NS - 1's loads are issued before tile n is
+    // computed, so NS - 1 tiles are in flight; the wait then lets exactly the
+    // loads issued after tile n stay in flight (none after the last tile, so
+    // no tile is fetched twice).  The compiler cannot count LDS-DMA
+    // completions, so the waits are explicit.  Tiles go round the ring in
+    // groups of NS so that every slot index is a compile-time constant.
+    static_for<0, NS - 1>([&](auto k_c) {
+      if (decltype(k_c)::value < nt) fetch(decltype(k_c)::value, k_c);
+    });
+    for (int n0 = 0; n0 < nt; n0 += NS) {
+      static_for<0, NS>([&](auto k_c) {
+        constexpr int K = decltype(k_c)::value;
+        const int n = n0 + K;
+        if (n < nt) {
+          if (n + NS - 1 < nt) fetch(n + NS - 1, std::integral_constant<int, (K + NS - 1) % NS>{});
+          wait_tiles_ahead<KV8 ? 4 : 8, NS - 1>(min(NS - 1, nt - 1 - n));
+          process(n, k_c);
+        }
+      });
     }
   }
   l = across_rows(l, OpSum());
@@ -720,6 +768,12 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 // ---------------------------------------------------------------------------
 namespace {
 
+// LDS ring slots per wave of the split-KV kernel (the single-pass kernel's
+// four waves keep two each).
+#ifndef PA_DECODE_SLOTS
+#define PA_DECODE_SLOTS 2
+#endif
+
 template <int G, int BS, bool KV8>
 hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.partition_size > 0) {
@@ -735,9 +789,9 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
     const dim3 fg = f.flat_units ? dim3(static_cast<unsigned>(nwg)) : grid;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, KV8>), fg, dim3(64), 0, s, f);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, KV8, PA_DECODE_SLOTS>), fg, dim3(64), 0, s, f);
   } else
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, KV8>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, KV8, 2>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

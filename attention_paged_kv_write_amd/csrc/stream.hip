@@ -43,20 +43,6 @@ __device__ __forceinline__ void lds_read_slot8(u32x4* w, uint32_t addr) {
 #endif
 }
 
-template <int AHEAD>
-__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
-  // at most `ahead` tiles (8 loads each) may stay in flight
-  if constexpr (AHEAD > 0) {
-    if (ahead >= AHEAD) {
-      wait_vmcnt<8 * AHEAD>();
-      return;
-    }
-    wait_tiles_ahead<AHEAD - 1>(ahead);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 }  // namespace
 
 // One wave per work unit (KV head, sequence, partition), bf16 rows of 128
@@ -125,7 +111,7 @@ __global__ __launch_bounds__(64) void paged_stream_kernel(DecodeArgs a, uint32_t
       for (int n = 0; n < DEPTH - 1 && n < nt; ++n) fetch(n);
       for (int n = 0; n < nt; ++n) {
         if (n + DEPTH - 1 < nt) fetch(n + DEPTH - 1);
-        wait_tiles_ahead<DEPTH - 1>(min(DEPTH - 1, nt - 1 - n));
+        wait_tiles_ahead<8, DEPTH - 1>(min(DEPTH - 1, nt - 1 - n));
         u32x4 w[8];
         lds_read_slot8(w, lds_addr(&ring[n % DEPTH][lane]));
         int pos0, lim;

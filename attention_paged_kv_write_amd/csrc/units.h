@@ -3,6 +3,8 @@
 // and the balanced flat order of units.
 #pragma once
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pa {
@@ -125,6 +127,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 #endif
+}
+
+// f(std::integral_constant<int, k>) for k = K .. N-1, unrolled (compile-time
+// indices, e.g. of LDS ring slots).
+template <int K, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<K + 1, N>(f);
+  }
+}
+
+// Wait until at most `ahead` (<= AHEAD, wave-uniform) tiles of PER loads each
+// are still in flight.
+template <int PER, int AHEAD>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (AHEAD > 0) {
+    if (ahead >= AHEAD) {
+      wait_vmcnt<PER * AHEAD>();
+      return;
+    }
+    wait_tiles_ahead<PER, AHEAD - 1>(ahead);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 }  // namespace pa
