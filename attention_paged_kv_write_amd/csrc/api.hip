@@ -5,10 +5,14 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
 #include "paged_attn.h"
+
+// The scratch array of paged_attention_decode_noalloc (see scratch_address).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[size_t(32) << 20];
 
 namespace {
 
@@ -43,6 +47,34 @@ bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 // Partition dimension of a split decode's partials.
 int split_parts(int max_context_len, int partition_size) {
   return max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+}
+
+// Scratch of paged_attention_decode_noalloc: the split partials live in this
+// file-scope device array, one copy per GPU, held until the process ends.  Host
+// code never passes the array's name (on the host it is only a stand-in): it
+// takes the address hipGetSymbolAddress gives for the current device, once per
+// device, and passes that.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use there).
+int scratch_address(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_LAUNCH, "%s: no current device (%s)", fn, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_LAUNCH, "%s: scratch address on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
 }
 
 // Host-side checks of a decode call (everything but the output pointers);
@@ -346,6 +378,42 @@ int paged_attention_decode_append_fp8(void* out, float* lse, float* part_out, fl
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, partition_size, max_context_len, scale, window, dtype, true, k_scale, v_scale,
                      stream);
+}
+
+int paged_attention_decode_noalloc(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, int partition_size, int max_context_len,
+                                   float scale, int window, pa_dtype dtype, void* stream) {
+  const char* fn = "paged_attention_decode_noalloc";
+  if (partition_size <= 0) return fail(PA_ERR_INVALID_ARG, "%s: partition_size must be > 0", fn);
+  int rc = decode_check(fn, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                        head_dim, block_size, max_blocks_per_seq, num_blocks, partition_size, max_context_len,
+                        scale, window, dtype, false, nullptr, nullptr);
+  if (rc != PA_OK) return rc;
+  const int P = split_parts(max_context_len, partition_size);
+  const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads * P;
+  const uint64_t out_bytes = (rows * head_dim * 4 + 255) / 256 * 256;
+  static_assert(sizeof(scratch) == kScratchBytes, "scratch size");
+  if (out_bytes + rows * 4 > kScratchBytes)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: partials need %llu bytes (num_seqs * num_q_heads * partitions * (head_dim + 1) * 4), "
+                "more than the %zu-byte scratch",
+                fn, static_cast<unsigned long long>(out_bytes + rows * 4), kScratchBytes);
+  if (num_seqs == 0) return ok();
+  if (!out || !lse) return fail(PA_ERR_INVALID_ARG, "%s: null out/lse", fn);
+  void* base = nullptr;
+  rc = scratch_address(fn, &base);
+  if (rc != PA_OK) return rc;
+  float* part_out = static_cast<float*>(base);
+  float* part_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + out_bytes);
+  rc = decode_call(fn, nullptr, nullptr, part_out, part_lse, q, nullptr, nullptr, k_cache, v_cache, block_tables,
+                   context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   num_blocks, partition_size, max_context_len, scale, window, dtype, false, nullptr, nullptr,
+                   stream);
+  if (rc != PA_OK) return rc;
+  return paged_attention_reduce_window(out, lse, part_out, part_lse, context_lens, num_seqs, num_q_heads, head_dim,
+                                       partition_size, P, window, dtype, stream);
 }
 
 int paged_attention_reduce(void* out, float* lse, const float* part_out, const float* part_lse,

@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
     "paged_attention_decode_fp8", "rope_cos_sin_cache", "paged_kv_write_rope",
     "paged_attention_decode_append", "paged_attention_decode_append_fp8", "paged_kv_stream_read",
+    "paged_attention_decode_noalloc",
 )
 PA_STREAM_LDS_DMA, PA_STREAM_REGISTERS = 0, 1
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
@@ -104,6 +105,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_prefill_window.restype = i32
     lib.paged_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.paged_attention_decode_noalloc.restype = i32
+    lib.paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                   i32, i32, f32, i32, i32, vp]
     lib.paged_kv_stream_read.restype = i32
     lib.paged_kv_stream_read.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                          i32, vp]
@@ -445,3 +449,30 @@ def paged_kv_stream_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tab
                                     block_tables.shape[1], NB, int(partition_size), int(max_context_len), int(mode),
                                     int(depth), _dtype_code(k_cache), _stream(k_cache)))
     return checksums
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                   scale: float, partition_size: int, out: torch.Tensor, lse: torch.Tensor,
+                                   window: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split decode and its merge in one library call that allocates nothing:
+    the partials live in the library's per-GPU scratch (at most 32 MiB of
+    them), so the caller passes only inputs and the outputs out [B, H_q, d]
+    and lse [B, H_q].  Calls that overlap on one GPU race on that scratch."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    B, Hq, d = q.shape
+    NB, Hkv, bs, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("paged_attention_decode_noalloc: inconsistent q / cache shapes or dtypes")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("paged_attention_decode_noalloc: block_tables / context_lens shape")
+    if out.shape != q.shape or lse.shape != (B, Hq):
+        raise ValueError("paged_attention_decode_noalloc: out must be [B, H_q, d] and lse [B, H_q]")
+    _check(lib.paged_attention_decode_noalloc(
+        _dev(out, "out", q.dtype, 3), _dev(lse, "lse", torch.float32, 2), _dev(q, "q", ndim=3),
+        _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+        B, Hq, Hkv, d, bs, block_tables.shape[1], NB, int(partition_size), int(max_context_len), float(scale),
+        int(window), dt, _stream(q)))
+    return out, lse

@@ -387,6 +387,37 @@ int paged_kv_write_rope(void* q, void* k, const void* v, void* k_cache, void* v_
                         int block_size, int num_blocks, int max_positions, pa_dtype dtype, void* stream);
 
 /*
+ * paged_attention_decode_noalloc - split-KV decode and its merge in one call
+ * that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * Computes exactly what paged_attention_decode_window with this partition_size
+ * followed by paged_attention_reduce_window computes (the same kernels), and
+ * writes out [B, H_q, d] (dtype) and lse [B, H_q] (float32).  The split
+ * partials do not come from the caller: they live in a scratch array inside
+ * the library, one per GPU, allocated with the library's code on that GPU and
+ * held until the process ends.  Limit: num_seqs * num_q_heads * P *
+ * (head_dim + 1) * 4 bytes (P = ceil(max_context_len / partition_size), the
+ * partials rounded up to 256 bytes) must fit in 32 MiB - e.g. 64 sequences x
+ * 32 heads x 8 partitions (8.5 MB) or 4 x 32 x 256 (16.9 MB) at head_dim 128;
+ * a larger call returns PA_ERR_INVALID_ARG and launches nothing.
+ * partition_size must be > 0 (a multiple of block_size).
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * on one GPU (on different streams, or from several threads without ordering)
+ * race and give undefined results.  The scratch needs no clearing: each call
+ * writes every partition it later reads.  Nothing is allocated or freed by
+ * the call itself; the first call on a device looks up that device's scratch
+ * address (hipGetSymbolAddress) and keeps it.
+ */
+int paged_attention_decode_noalloc(void* out, float* lse, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, int partition_size, int max_context_len, float scale,
+                                   int window, pa_dtype dtype, void* stream);
+
+/*
  * paged_kv_stream_read - a measurement call, not a step of the method: the
  * bandwidth ceiling of the split-KV decode's memory access pattern.
  *
