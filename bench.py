@@ -191,7 +191,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition-size", type=int, default=256)
+    ap.add_argument("--partition-size", type=int, default=1024,
+                    help="split-KV partition of the headline decode step (the fastest of those timed in "
+                         "roofline.partition_size_variants on MI355X)")
+    ap.add_argument("--fp8-partition-size", type=int, default=256)
     ap.add_argument("--copies", type=int, default=3, help="independent input copies rotated per step")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
@@ -343,7 +346,7 @@ def main(argv=None):
     # The same decode kernel at other partition sizes (0 = one pass per
     # (sequence, KV head) writing out/lse directly, no reduce needed).
     variants = {}
-    for vps in sorted({0, 128, 256, 512} - {ps}):
+    for vps in sorted({0, 256, 512, 768, 1024} - {ps}):
         vP = ops.num_partitions(maxctx, vps) if vps else 1
         vbuf = [dict(po=torch.empty((B, Hq, vP, d), dtype=torch.float32, device=dev),
                      pl=torch.empty((B, Hq, vP), dtype=torch.float32, device=dev)) if vps else None
@@ -676,7 +679,8 @@ def main(argv=None):
         fB, fHq, fHkv, fd = fc.spec.batch, fc.spec.num_q_heads, fc.spec.num_kv_heads, fc.spec.head_dim
         log(f"fp8 workload generated in {time.perf_counter() - t0:.1f}s: NB={fc.num_blocks}")
         fbytes = int(fc.context_lens.astype(np.int64).sum()) * fHkv * 2 * fd   # one byte per element
-        fP = ops.num_partitions(fc.max_context_len, ps)
+        fps = args.fp8_partition_size
+        fP = ops.num_partitions(fc.max_context_len, fps)
         # the newest token of each sequence (its last row of the written history)
         last = np.cumsum(fc.context_lens.astype(np.int64)) - 1
         ks_d = torch.tensor([fc.k_scale], dtype=torch.float32, device=dev)
@@ -710,13 +714,13 @@ def main(argv=None):
 
         def fdecode(c):
             ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], fc.max_context_len, fc.scale,
-                                       ps, part_out=c["po"], part_lse=c["pl"], k_scale=ks_d, v_scale=vs_d)
+                                       fps, part_out=c["po"], part_lse=c["pl"], k_scale=ks_d, v_scale=vs_d)
 
         def fstep(c):
             ops.paged_attention_decode(c["q"], c["kc"], c["vc"], c["bt"], c["cl"], fc.max_context_len, fc.scale,
-                                       ps, part_out=c["po"], part_lse=c["pl"], k_scale=ks_d, v_scale=vs_d,
+                                       fps, part_out=c["po"], part_lse=c["pl"], k_scale=ks_d, v_scale=vs_d,
                                        k_new=c["kn"], v_new=c["vn"])
-            ops.paged_attention_reduce(c["po"], c["pl"], c["cl"], ps, out=c["out"], lse=c["lse"])
+            ops.paged_attention_reduce(c["po"], c["pl"], c["cl"], fps, out=c["out"], lse=c["lse"])
 
         def ftimed(fn, n_groups):
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -737,7 +741,7 @@ def main(argv=None):
         favg = float(np.mean(fdec_ms))
         fgbs = fbytes / (favg * 1e-3) / 1e9
         fsms = float(np.mean(fstep_ms))
-        fp8 = {"workload": fc.spec.name, "partition_size": ps, "k_scale": fc.k_scale, "v_scale": fc.v_scale,
+        fp8 = {"workload": fc.spec.name, "partition_size": fps, "k_scale": fc.k_scale, "v_scale": fc.v_scale,
                "sum_context": int(fc.context_lens.sum()), "kv_bytes_per_step": fbytes,
                "step_us": round(fsms * 1e3, 2), "step_gbs": round(fbytes / (fsms * 1e-3) / 1e9, 1),
                "decode_tokens_per_s": round(fB / (fsms * 1e-3), 1),
