@@ -16,11 +16,14 @@
 // depends only on logical positions, never on physical block ids, so
 // permuting the pool leaves every result bit-identical.
 //
-// Two kernels:
+// Three kernels:
 //  * decode_mfma_kernel (bf16, head_dim 128): K and V tiles of 16 tokens are
 //    staged in LDS by LDS-DMA; QK^T against the whole GQA group is a chain of
 //    four v_mfma_f32_16x16x32_bf16 and P.V eight v_mfma_f32_16x16x16_bf16 (see
 //    the comment above the kernel).
+//  * decode_fp8_kernel (E4M3 pools, head_dim 128): the same scheme over
+//    32-row steps, codes converted to bf16 operands in registers, V^T read
+//    straight from the code tile by transposed byte reads.
 //  * decode_generic_kernel (fp32 or bf16, head_dim 64/128): vector ALU only;
 //    LPT lanes share a token row, dot products reduced with DPP.
 #include "kernels.h"
@@ -330,52 +333,36 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
 #endif
 }
 
-// FP8 tile, first step: this lane's 32 K codes and 32 V codes (two 16-byte
-// reads each) from its LDS ring slot (byte offset OFF), then wait for them.
+// FP8 step: this lane's 64 K codes (two 16-byte reads per tile) and its eight
+// transposed V reads (8 codes each) from its LDS ring slot (byte offset OFF),
+// then wait for them (inline asm for the same reason as the bf16 tile read).
 template <int OFF>
-__device__ __forceinline__ void lds_read_fp8_tile(u32x4* k8, u32x4* v8, const uint32_t* k_addr,
+__device__ __forceinline__ void lds_read_fp8_step(u32x4* k8, u32x2* v8, const uint32_t* k_addr,
                                                   const uint32_t* v_addr) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n\t"
-      "ds_read_b128 %1, %5 offset:%8\n\t"
-      "ds_read_b128 %2, %6 offset:%8\n\t"
-      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "ds_read_b128 %0, %12 offset:%24\n\t"
+      "ds_read_b128 %1, %13 offset:%24\n\t"
+      "ds_read_b128 %2, %14 offset:%24\n\t"
+      "ds_read_b128 %3, %15 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %4, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %5, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %6, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %9, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %10, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b8 %11, %23 offset:%24\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k8[0]), "=&v"(k8[1]), "=&v"(v8[0]), "=&v"(v8[1])
-      : "v"(k_addr[0]), "v"(k_addr[1]), "v"(v_addr[0]), "v"(v_addr[1]), "i"(OFF)
+      : "=&v"(k8[0]), "=&v"(k8[1]), "=&v"(k8[2]), "=&v"(k8[3]), "=&v"(v8[0]), "=&v"(v8[1]),
+        "=&v"(v8[2]), "=&v"(v8[3]), "=&v"(v8[4]), "=&v"(v8[5]), "=&v"(v8[6]), "=&v"(v8[7])
+      : "v"(k_addr[0]), "v"(k_addr[1]), "v"(k_addr[2]), "v"(k_addr[3]), "v"(v_addr[0]), "v"(v_addr[1]),
+        "v"(v_addr[2]), "v"(v_addr[3]), "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7]),
+        "i"(OFF)
       : "memory");
 #endif
 }
 
-// FP8 tile, second step: store this lane's 32 converted V values (bf16) into
-// the wave's staging tile, wait, then the eight transposed reads of V^T.
-__device__ __forceinline__ void lds_stage_v_read_tr(const u32x4* vb, const uint32_t* st_addr, u32x2* vt,
-                                                    const uint32_t* v_addr) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile(
-      "ds_write_b128 %8, %12\n\t"
-      "ds_write_b128 %9, %13\n\t"
-      "ds_write_b128 %10, %14\n\t"
-      "ds_write_b128 %11, %15\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %18\n\t"
-      "ds_read_b64_tr_b16 %3, %19\n\t"
-      "ds_read_b64_tr_b16 %4, %20\n\t"
-      "ds_read_b64_tr_b16 %5, %21\n\t"
-      "ds_read_b64_tr_b16 %6, %22\n\t"
-      "ds_read_b64_tr_b16 %7, %23\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vt[0]), "=&v"(vt[1]), "=&v"(vt[2]), "=&v"(vt[3]), "=&v"(vt[4]), "=&v"(vt[5]),
-        "=&v"(vt[6]), "=&v"(vt[7])
-      : "v"(st_addr[0]), "v"(st_addr[1]), "v"(st_addr[2]), "v"(st_addr[3]), "v"(vb[0]), "v"(vb[1]),
-        "v"(vb[2]), "v"(vb[3]), "v"(v_addr[0]), "v"(v_addr[1]), "v"(v_addr[2]), "v"(v_addr[3]),
-        "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7])
-      : "memory");
-#endif
-}
 
 // Eight E4M3 codes (two dwords) -> eight bf16 (exact: every E4M3 value is a
 // bf16 value), low byte first.  The convert's scale operand is 1.
@@ -388,342 +375,56 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// MFMA kernel: bf16, head_dim 128, block_size a multiple of 16
-// ---------------------------------------------------------------------------
-// W waves per workgroup: W = 1 in split-KV mode (one wave owns one partition,
-// so every work unit of a launch can be resident at once and no cross-wave
-// merge is needed); W = 4 for the single-pass mode (the waves take the
-// sequence's blocks round-robin and meet in LDS).
-//
-// Per 16-token tile of KV head g:
-//   S^T[16 tok x 16 col] = K[16 x 128] . Q^T   four v_mfma_f32_16x16x32_bf16;
-//       lane (j, c16) reads token c16, dims 32c + 8j of the K tile as its A
-//       operand, the group's query heads are the B operand columns.
-//   online softmax on S^T: lane (j, c16) holds tokens 4j..4j+3 of column c16,
-//       so the running max/rescale of a column stay in its own lanes; the tile
-//       max needs one exchange across the four 16-lane rows.
-//   O^T[128 d x 16 col] += V^T . P^T   eight v_mfma_f32_16x16x16_bf16: the
-//       S^T accumulator layout is exactly the P^T B operand (4 consecutive
-//       tokens of one column per lane), and V^T comes from LDS through
-//       ds_read_b64_tr_b16, which hands each lane 4 consecutive tokens of one
-//       dim from a row-major V tile.
-// K and V tiles reach LDS by non-temporal global_load_lds_dwordx4 (no VGPRs;
-// every cache byte is read once) into a two-slot ring per wave, so one tile's
-// loads are in flight while the other is computed.  Both tiles are stored
-// row-major with XOR-swizzled 16-byte chunks: K chunk q of token t at q ^ t
-// (conflict-free lane-linear b128 reads), V at q ^ 2*(t%8) (the eight tokens a
-// transposed read touches spread over all 64 banks).
-//
-// KV8: the pools hold E4M3 codes (half the bytes).  A ring slot holds the K
-// and V tiles as codes (2 KB each, row-major, chunk q of token t at
-// q ^ (t/2): conflict-free 16-byte reads of 128-byte rows).  K: the dot
-// product's dims are taken in a permuted order so that MFMA c, lane (j, c16)
-// uses dims 32j + 8c .. +7 of token c16 (Q is loaded in the same order):
-// each lane's 32 dims are one contiguous 32-byte run, read with two
-// ds_read_b128 and converted to bf16 operands.  V: lane l converts dims
-// 32(l%4) .. +31 of token l/4 to bf16 into a per-wave staging tile laid out
-// like the bf16 V tile, which the transposed reads then use unchanged.  The
-// K scale multiplies the softmax scale, the V scale the output.
-template <int G, int BS, int W, bool KV8, int NS>
-__global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int D = 128;
-  constexpr int RC = D * 2 / 16;   // 16-byte chunks per bf16 row (16)
-  constexpr int RC8 = D / 16;      // 16-byte chunks per E4M3 row (8)
-  constexpr int TPB = BS / 16;     // 16-token tiles per block
-  typedef short short4v __attribute__((ext_vector_type(4)));
 
-  // LDS ring, per slot and wave: K tile (4 KB, MFMA A layout, lane-linear)
-  // then V tile (4 KB, row-major, chunk-swizzled); KV8: 2 KB each, plus the
-  // bf16 V staging tile
-  constexpr int kSlotChunks = KV8 ? 256 : 512;
-  constexpr int kSlotBytes = kSlotChunks * 16;
-  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][kSlotChunks];
-  __shared__ __attribute__((aligned(16))) u32x4 stage[KV8 ? W : 1][KV8 ? 256 : 1];
-  __shared__ float sm_m[W][G];
-  __shared__ float sm_l[W][G];
-  __shared__ float sm_acc[W > 1 ? W : 1][G][D];
-
+// ---------------------------------------------------------------------------
+// Pieces shared by the two MFMA kernels (head_dim 128, one GQA group of G
+// query heads per wave as the 16 columns of the matrix products)
+// ---------------------------------------------------------------------------
+// The work unit of this workgroup: KV head g, sequence b, partition part.
+// W == 1 with a flat grid: the balanced unit of the id (b = -1 past the
+// last unit); otherwise the grid coordinates.
+struct UnitId {
   int g, b, part;
+};
+template <int W>
+__device__ __forceinline__ UnitId unit_id(const DecodeArgs& a) {
   if (W == 1 && a.flat_units) {
-    g = blockIdx.x % a.num_kv_heads;
     const Unit un = flat_unit(a, blockIdx.x / a.num_kv_heads);
-    if (un.b < 0) return;
-    b = __builtin_amdgcn_readfirstlane(un.b);
-    part = __builtin_amdgcn_readfirstlane(un.part);
-  } else {
-    g = blockIdx.x;
-    b = blockIdx.y;
-    part = blockIdx.z;
+    if (un.b < 0) return {0, -1, 0};
+    return {static_cast<int>(blockIdx.x % a.num_kv_heads), __builtin_amdgcn_readfirstlane(un.b),
+            __builtin_amdgcn_readfirstlane(un.part)};
   }
-  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-  const int lane = threadIdx.x & 63;
+  return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
+}
+
+// The group's queries as the B operand of the four QK^T MFMAs: column c16 is
+// query head g*G + c16 (zero past G); MFMA c takes 16-byte chunk 4c + j of
+// the bf16 row, or chunk 4j + c when the dims run in the E4M3 kernel's
+// permuted order.  qsign flips the sign bits (a negative softmax scale).
+template <int G, bool PERMUTED>
+__device__ __forceinline__ void load_group_queries(const DecodeArgs& a, int b, int g, int j, int c16,
+                                                   uint32_t qsign, bf16x8* qf) {
+  constexpr int RC = 16;   // 16-byte chunks per bf16 row of 128
+  const u32x4* qc = static_cast<const u32x4*>(a.q);
+  const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (c16 < G) w = qc[row * RC + (PERMUTED ? 4 * j + c : 4 * c + j)] ^ qsign;
+    qf[c] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// The end of a work unit: the running sum of column c16 gathered over the four
+// 16-lane rows, then O / l (times vsc, the V scale of an E4M3 pool) and the
+// log-sum-exp stored as the unit's partial result (split mode), or as the
+// final result (single pass: W == 1) or merged across the W waves in LDS first.
+template <int G, int W>
+__device__ __forceinline__ void finish_unit(const DecodeArgs& a, int b, int g, int part, int wave, int lane,
+                                            float m, float l, const floatx4* oacc, float vsc,
+                                            float (*sm_m)[G], float (*sm_l)[G], float (*sm_acc)[G][128]) {
+  constexpr int D = 128;
   const int j = lane >> 4, c16 = lane & 15;
-  const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
-  const int blk_lo = a.partition_size > 0 ? part * (a.partition_size / BS) : 0;
-
-  // First round trip: context length, the group's queries, and the first
-  // window of block ids (speculative: bounded by the table row, masked below).
-  const int ctx_raw = a.context_lens[b];
-  // The softmax scale (times the K scale of an E4M3 pool) multiplies the raw
-  // scores inside the exponent's FMA and the tile max only (max(s) * c =
-  // max(s * c) for c > 0); a negative scale is folded into Q by an exact sign
-  // flip of its bf16 values, and a zero one becomes the smallest normal float
-  // so that masked scores stay -inf.
-  const float sl2_raw = KV8 ? a.scale_log2 * a.k_scale[0] : a.scale_log2;
-  const float sl2 = fmaxf(fabsf(sl2_raw), 1.17549435e-38f);
-  const uint32_t qsign = sl2_raw < 0.f ? 0x80008000u : 0u;
-  bf16x8 qf[4];
-  {
-    const u32x4* qc = static_cast<const u32x4*>(a.q);
-    const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (c16 < G) w = qc[row * RC + (KV8 ? 4 * j + c : 4 * c + j)] ^ qsign;
-      qf[c] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-  int ids_lo = blk_lo;   // first block of the id window; moves up under a window
-  auto load_ids = [&](int w0) -> int {
-    const int e = ids_lo + wave + W * (w0 + lane);
-    return e < a.max_blocks_per_seq ? table[e] : -1;
-  };
-  int ids = load_ids(0);
-
-  const Range r = work_range(a, b, part);
-  (void)ctx_raw;
-  if (r.blk_lo >= r.blk_hi) {
-    if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
-    return;
-  }
-  // a sliding window starts the span past the speculated first block
-  if (r.blk_lo != ids_lo) {
-    ids_lo = r.blk_lo;
-    ids = load_ids(0);
-  }
-  {
-    const int lblk = append_block(a, r, wave, W);
-    if (lblk >= 0) {
-      const int phys = table[lblk];
-      if (phys >= 0 && phys < a.num_blocks) append_new_token<D, 2, KV8>(a, b, g, phys, (r.ctx - 1) % BS, lane);
-    }
-  }
-  const int span = r.blk_hi - r.blk_lo;
-  const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;
-
-  float m = kNegInf;   // running max (log2 units) of column c16
-  float l = 0.f;       // this lane's share of the running sum of column c16
-  floatx4 oacc[8];     // O^T: dims 16dn + 4j + i of column c16
-#pragma unroll
-  for (int dn = 0; dn < 8; ++dn) oacc[dn] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
-  const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
-
-  // transposed-read address pieces (constant per lane): token 4j + c16/4,
-  // dims 16dn + 4(c16%4) .. +3
-  // (the chunk of dims 16dn + 4(c16%4) is 2dn + tr_half, stored at
-  // (2dn + tr_half) ^ 2*(tok%8) = 2*(dn ^ tr_t8) + tr_half)
-  const int tr_tok = 4 * j + (c16 >> 2);
-  const int tr_t8 = tr_tok & 7;
-  const int tr_half = (c16 & 3) >> 1;   // which 8-dim chunk of the 16-dim group
-  const int tr_off = 8 * (c16 & 1);     // byte offset inside the 16-byte chunk
-  // slot-0 LDS addresses of this lane's reads (other slots: + slot * kSlotBytes)
-  // K row t, dim chunk q is stored at chunk q ^ t of the slot's row t; the MFMA
-  // A operand of instruction c wants row c16, chunk 4c + j
-  uint32_t k_addr[4];
-  uint32_t v_addr[8];
-  uint32_t k8_addr[2], v8_addr[2], st_addr[4];   // KV8 only
-  if constexpr (!KV8) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) k_addr[c] = lds_addr(&ring[wave][0][16 * c16 + ((4 * c + j) ^ c16)]);
-#pragma unroll
-    for (int dn = 0; dn < 8; ++dn)
-      v_addr[dn] = lds_addr(&ring[wave][0][256]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
-  } else {
-    // K codes: token c16, chunks 2j and 2j+1 (stored at q ^ (c16/2))
-#pragma unroll
-    for (int e = 0; e < 2; ++e) k8_addr[e] = lds_addr(&ring[wave][0][8 * c16 + ((2 * j + e) ^ (c16 >> 1))]);
-    // V codes to convert: token lane/4, chunks 2(lane%4) and +1
-    const int vtok = lane >> 2, vq = 2 * (lane & 3);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      v8_addr[e] = lds_addr(&ring[wave][0][128 + 8 * vtok + ((vq + e) ^ (vtok >> 1))]);
-    // their bf16 chunks 4(lane%4) + u in the staging tile, swizzled like the bf16 V tile
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st_addr[u] = lds_addr(&stage[wave][16 * vtok + ((4 * (lane & 3) + u) ^ (2 * (vtok & 7)))]);
-#pragma unroll
-    for (int dn = 0; dn < 8; ++dn)
-      v_addr[dn] = lds_addr(&stage[wave][0]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
-  }
-  // E4M3: the V scale multiplies the output
-  const float vsc = KV8 ? a.v_scale[0] : 1.f;
-  // Per-lane byte offsets of the tile's LDS-DMA loads from the (wave-uniform)
-  // start of its rows: row 4c + j (K) / 4k + j (V) at its swizzled chunk;
-  // E4M3: row 8i + lane/8.  Opaque, so that each load is a scalar base plus
-  // this 32-bit offset rather than 64-bit address arithmetic per load.
-  uint32_t dma_off[8];
-  if constexpr (!KV8) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int tok = 4 * c + j;
-      dma_off[c] = static_cast<uint32_t>((tok * RC + (c16 ^ tok)) * 16);
-      dma_off[4 + c] = static_cast<uint32_t>((tok * RC + (c16 ^ (2 * (tok & 7)))) * 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = 8 * i + (lane >> 3);
-      dma_off[i] = static_cast<uint32_t>((tok * RC8 + ((lane & 7) ^ (tok >> 1))) * 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
-
-  for (int w0 = 0; w0 < n_blocks; w0 += 64) {
-    if (w0 > 0) ids = load_ids(w0);
-    const int wn = min(64, n_blocks - w0);
-    const int nt = wn * TPB;
-
-    // Window tile n: first token position and the valid-token limit (0 when
-    // the block id lies outside the pool, a precondition violation: block 0 is
-    // read instead and every token masked).
-    auto tile_span = [&](int n, int& pos0, int& lim, int& phys) {
-      const int i = n / TPB;
-      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + (n % TPB) * 16;
-      phys = __builtin_amdgcn_readlane(ids, i);
-      const bool ok = phys >= 0 && phys < a.num_blocks;
-      phys = ok ? phys : 0;
-      lim = ok ? r.ctx : 0;
-    };
-    // Issue the LDS-DMA loads of window tile n into ring slot SLOT (K then V,
-    // both row-major with the XOR chunk swizzle).
-    auto fetch = [&](int n, auto slot_c) {
-      constexpr int SLOT = decltype(slot_c)::value;
-      int pos0, lim, phys;
-      tile_span(n, pos0, lim, phys);
-      if constexpr (KV8) {
-        // 16 rows x 8 chunks per tile and pool: two loads of 64 chunks each
-        const size_t base8 = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC8;
-        const char* kb = reinterpret_cast<const char*>(kc + base8);
-        const char* vb = reinterpret_cast<const char*>(vc + base8);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          global_to_lds16<PA_DECODE_AUX>(kb + dma_off[i], &ring[wave][SLOT][64 * i]);
-          global_to_lds16<PA_DECODE_AUX>(vb + dma_off[i], &ring[wave][SLOT][128 + 64 * i]);
-        }
-        return;
-      }
-      const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC;
-      const char* kb = reinterpret_cast<const char*>(kc + base);
-      const char* vb = reinterpret_cast<const char*>(vc + base);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) global_to_lds16<PA_DECODE_AUX>(kb + dma_off[c], &ring[wave][SLOT][64 * c]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) global_to_lds16<PA_DECODE_AUX>(vb + dma_off[4 + k], &ring[wave][SLOT][256 + 64 * k]);
-    };
-
-    // Compute window tile n from ring slot SLOT (its loads have landed).
-    auto process = [&](int n, auto slot_c) {
-      constexpr int OFF = decltype(slot_c)::value * kSlotBytes;
-      int pos0, lim, phys;
-      tile_span(n, pos0, lim, phys);
-      u32x4 kw[4];
-      u32x2 vt[8];
-      // Rows past the end of the sequence may hold anything (NaN), and a zero
-      // probability times NaN is still NaN: in the tile that holds the end,
-      // each lane zeroes the V rows it fetched that lie past it (in LDS,
-      // before the reads; LDS operations of a wave complete in order).
-      if (pos0 + 16 > lim) {
-        constexpr int SLOT = decltype(slot_c)::value;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        if constexpr (!KV8) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (pos0 + 4 * k + j >= lim) ring[wave][SLOT][256 + 64 * k + lane] = zero;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            if (pos0 + 8 * i + (lane >> 3) >= lim) ring[wave][SLOT][128 + 64 * i + lane] = zero;
-        }
-      }
-      if constexpr (!KV8) {
-        lds_read_decode_tile<OFF>(kw, vt, k_addr, v_addr);
-      } else {
-        u32x4 k8[2], v8[2];
-        lds_read_fp8_tile<OFF>(k8, v8, k8_addr, v8_addr);
-        u32x4 vb[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) vb[u] = e4m3x8_to_bf16(v8[u >> 1][2 * (u & 1)], v8[u >> 1][2 * (u & 1) + 1]);
-        lds_stage_v_read_tr(vb, st_addr, vt, v_addr);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kw[c] = e4m3x8_to_bf16(k8[c >> 1][2 * (c & 1)], k8[c >> 1][2 * (c & 1) + 1]);
-      }
-      floatx4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[c]), qf[c], st, 0, 0, 0);
-      // st[i]: raw score of token pos0 + 4j + i for column c16.  A tile wholly
-      // inside the visible range (the common case) takes no mask; the others
-      // set their invisible scores to -inf (a wave-uniform branch).
-      const bool full = pos0 >= r.lo && pos0 + 16 <= lim;
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = st[i];
-      if (!full) {
-        int d0 = pos0 + 4 * j;
-        asm volatile("" : "+v"(d0));   // keeps the compares out of full tiles
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = (d0 + i < lim && d0 + i >= r.lo) ? s[i] : kNegInf;
-      }
-      // IEEE maximum (v_maximum3_f32): compiler-visible, so its reads of the
-      // matrix-core results are ordered by the compiler
-      auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
-      const float mx = quarter_max(mx2(mx2(s[0], s[1]), mx2(s[2], s[3]))) * sl2;
-      // lazy rescale: the running max moves (with l and O) only when some
-      // column's tile max exceeds it by more than the slack
-      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
-        m = m_new;
-        l *= alpha;
-#pragma unroll
-        for (int dn = 0; dn < 8; ++dn) oacc[dn] *= alpha;
-      }
-      const float ms = m == kNegInf ? 0.f : m;   // no visible token yet (bad block ids)
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(s[i], sl2, -ms));   // masked: exp2(-inf) = 0
-      l += (p[0] + p[1]) + (p[2] + p[3]);
-      const short4v pb = __builtin_bit_cast(short4v, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-#pragma unroll
-      for (int dn = 0; dn < 8; ++dn)
-        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, vt[dn]), pb, oacc[dn], 0,
-                                                              0, 0);
-    };
-    // Ring of NS slots: tile n + NS - 1's loads are issued before tile n is
-    // computed, so NS - 1 tiles are in flight; the wait then lets exactly the
-    // loads issued after tile n stay in flight (none after the last tile, so
-    // no tile is fetched twice).  The compiler cannot count LDS-DMA
-    // completions, so the waits are explicit.  Tiles go round the ring in
-    // groups of NS so that every slot index is a compile-time constant.
-    static_for<0, NS - 1>([&](auto k_c) {
-      if (decltype(k_c)::value < nt) fetch(decltype(k_c)::value, k_c);
-    });
-    for (int n0 = 0; n0 < nt; n0 += NS) {
-      static_for<0, NS>([&](auto k_c) {
-        constexpr int K = decltype(k_c)::value;
-        const int n = n0 + K;
-        if (n < nt) {
-          if (n + NS - 1 < nt) fetch(n + NS - 1, std::integral_constant<int, (K + NS - 1) % NS>{});
-          wait_tiles_ahead<KV8 ? 4 : 8, NS - 1>(min(NS - 1, nt - 1 - n));
-          process(n, k_c);
-        }
-      });
-    }
-  }
   l = across_rows(l, OpSum());
   if constexpr (W == 1) {
     if (c16 >= G) return;
@@ -763,15 +464,512 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   }
 }
 
+// Online-softmax update of one column (lane (j, c16) holds N raw scores of
+// column c16, invisible ones -inf): the step max over the four 16-lane rows,
+// a lazy rescale of (m, l, O) when some column's max passes m by more than
+// the slack, then the probabilities exp2(s * sl2 - m) into p and their sum
+// into l.  sl2 > 0 multiplies the raw scores inside the exponent's FMA and
+// the max only (max(s) * c = max(s * c) for c > 0).
+template <int N>
+__device__ __forceinline__ void softmax_step(const float* s, float sl2, float& m, float& l, floatx4* oacc,
+                                             float* p) {
+  // IEEE maximum (v_maximum3_f32): compiler-visible, so its reads of the
+  // matrix-core results are ordered by the compiler
+  auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+  float t = mx2(mx2(s[0], s[1]), mx2(s[2], s[3]));
+  if constexpr (N == 8) t = mx2(t, mx2(mx2(s[4], s[5]), mx2(s[6], s[7])));
+  const float mx = quarter_max(t) * sl2;
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dn = 0; dn < 8; ++dn) oacc[dn] *= alpha;
+  }
+  const float ms = m == kNegInf ? 0.f : m;   // no visible token yet (bad block ids)
+#pragma unroll
+  for (int i = 0; i < N; ++i) p[i] = fast_exp2(fmaf(s[i], sl2, -ms));   // masked: exp2(-inf) = 0
+  float sum = (p[0] + p[1]) + (p[2] + p[3]);
+  if constexpr (N == 8) sum += (p[4] + p[5]) + (p[6] + p[7]);
+  l += sum;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel: bf16, head_dim 128, block_size a multiple of 16
+// ---------------------------------------------------------------------------
+// W waves per workgroup: W = 1 in split-KV mode (one wave owns one partition,
+// so every work unit of a launch can be resident at once and no cross-wave
+// merge is needed); W = 4 for the single-pass mode (the waves take the
+// sequence's blocks round-robin and meet in LDS).
+//
+// Per 16-token tile of KV head g:
+//   S^T[16 tok x 16 col] = K[16 x 128] . Q^T   four v_mfma_f32_16x16x32_bf16;
+//       lane (j, c16) reads token c16, dims 32c + 8j of the K tile as its A
+//       operand, the group's query heads are the B operand columns.
+//   online softmax on S^T: lane (j, c16) holds tokens 4j..4j+3 of column c16,
+//       so the running max/rescale of a column stay in its own lanes; the tile
+//       max needs one exchange across the four 16-lane rows.
+//   O^T[128 d x 16 col] += V^T . P^T   eight v_mfma_f32_16x16x16_bf16: the
+//       S^T accumulator layout is exactly the P^T B operand (4 consecutive
+//       tokens of one column per lane), and V^T comes from LDS through
+//       ds_read_b64_tr_b16, which hands each lane 4 consecutive tokens of one
+//       dim from a row-major V tile.
+// K and V tiles reach LDS by non-temporal global_load_lds_dwordx4 (no VGPRs;
+// every cache byte is read once) into a ring of NS slots per wave, so NS - 1
+// tiles' loads are in flight while one is computed.  Both tiles are stored
+// row-major with XOR-swizzled 16-byte chunks: K chunk q of token t at q ^ t
+// (conflict-free lane-linear b128 reads), V at q ^ 2*(t%8) (the eight tokens a
+// transposed read touches spread over all 64 banks).
+template <int G, int BS, int W, int NS>
+__global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int RC = D * 2 / 16;   // 16-byte chunks per bf16 row (16)
+  constexpr int TPB = BS / 16;     // 16-token tiles per block
+  typedef short short4v __attribute__((ext_vector_type(4)));
+
+  // LDS ring, per slot and wave: K tile (4 KB) then V tile (4 KB)
+  constexpr int kSlotChunks = 512;
+  constexpr int kSlotBytes = kSlotChunks * 16;
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][kSlotChunks];
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  __shared__ float sm_acc[W > 1 ? W : 1][G][D];
+
+  const UnitId u = unit_id<W>(a);
+  if (u.b < 0) return;
+  const int g = u.g, b = u.b, part = u.part;
+  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4, c16 = lane & 15;
+  const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  const int blk_lo = a.partition_size > 0 ? part * (a.partition_size / BS) : 0;
+
+  // First round trip: the group's queries and the first window of block ids
+  // (speculative: bounded by the table row, masked below), issued before the
+  // context length is needed.  The softmax scale multiplies the raw scores
+  // inside the exponent's FMA and the tile max only; a negative scale is
+  // folded into Q by an exact sign flip of its bf16 values, and a zero one
+  // becomes the smallest normal float so that masked scores stay -inf.
+  const float sl2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  bf16x8 qf[4];
+  load_group_queries<G, false>(a, b, g, j, c16, qsign, qf);
+  int ids_lo = blk_lo;   // first block of the id window; moves up under a window
+  auto load_ids = [&](int w0) -> int {
+    const int e = ids_lo + wave + W * (w0 + lane);
+    return e < a.max_blocks_per_seq ? table[e] : -1;
+  };
+  int ids = load_ids(0);
+
+  const Range r = work_range(a, b, part);
+  if (r.blk_lo >= r.blk_hi) {
+    if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
+    return;
+  }
+  // a sliding window starts the span past the speculated first block
+  if (r.blk_lo != ids_lo) {
+    ids_lo = r.blk_lo;
+    ids = load_ids(0);
+  }
+  {
+    const int lblk = append_block(a, r, wave, W);
+    if (lblk >= 0) {
+      const int phys = table[lblk];
+      if (phys >= 0 && phys < a.num_blocks) append_new_token<D, 2, false>(a, b, g, phys, (r.ctx - 1) % BS, lane);
+    }
+  }
+  const int span = r.blk_hi - r.blk_lo;
+  const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;
+
+  float m = kNegInf;   // running max (log2 units) of column c16
+  float l = 0.f;       // this lane's share of the running sum of column c16
+  floatx4 oacc[8];     // O^T: dims 16dn + 4j + i of column c16
+#pragma unroll
+  for (int dn = 0; dn < 8; ++dn) oacc[dn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
+  const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
+
+  // transposed-read address pieces (constant per lane): token 4j + c16/4,
+  // dims 16dn + 4(c16%4) .. +3
+  // (the chunk of dims 16dn + 4(c16%4) is 2dn + tr_half, stored at
+  // (2dn + tr_half) ^ 2*(tok%8) = 2*(dn ^ tr_t8) + tr_half)
+  const int tr_tok = 4 * j + (c16 >> 2);
+  const int tr_t8 = tr_tok & 7;
+  const int tr_half = (c16 & 3) >> 1;   // which 8-dim chunk of the 16-dim group
+  const int tr_off = 8 * (c16 & 1);     // byte offset inside the 16-byte chunk
+  // slot-0 LDS addresses of this lane's reads (other slots: + slot * kSlotBytes)
+  // K row t, dim chunk q is stored at chunk q ^ t of the slot's row t; the MFMA
+  // A operand of instruction c wants row c16, chunk 4c + j
+  uint32_t k_addr[4];
+  uint32_t v_addr[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_addr[c] = lds_addr(&ring[wave][0][16 * c16 + ((4 * c + j) ^ c16)]);
+#pragma unroll
+  for (int dn = 0; dn < 8; ++dn)
+    v_addr[dn] = lds_addr(&ring[wave][0][256]) + tr_tok * 256 + tr_off + tr_half * 16 + 32 * (dn ^ tr_t8);
+  // Per-lane byte offsets of the tile's LDS-DMA loads from the (wave-uniform)
+  // start of its rows: row 4c + j (K) / 4k + j (V) at its swizzled chunk.
+  // Opaque, so that each load is a scalar base plus this 32-bit offset rather
+  // than 64-bit address arithmetic per load.
+  uint32_t dma_off[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int tok = 4 * c + j;
+    dma_off[c] = static_cast<uint32_t>((tok * RC + (c16 ^ tok)) * 16);
+    dma_off[4 + c] = static_cast<uint32_t>((tok * RC + (c16 ^ (2 * (tok & 7)))) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
+
+  for (int w0 = 0; w0 < n_blocks; w0 += 64) {
+    if (w0 > 0) ids = load_ids(w0);
+    const int wn = min(64, n_blocks - w0);
+    const int nt = wn * TPB;
+
+    // Window tile n: first token position and the valid-token limit (0 when
+    // the block id lies outside the pool, a precondition violation: block 0 is
+    // read instead and every token masked).
+    auto tile_span = [&](int n, int& pos0, int& lim, int& phys) {
+      const int i = n / TPB;
+      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + (n % TPB) * 16;
+      phys = __builtin_amdgcn_readlane(ids, i);
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      phys = ok ? phys : 0;
+      lim = ok ? r.ctx : 0;
+    };
+    // Issue the LDS-DMA loads of window tile n into ring slot SLOT (K then V,
+    // both row-major with the XOR chunk swizzle).
+    auto fetch = [&](int n, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      int pos0, lim, phys;
+      tile_span(n, pos0, lim, phys);
+      const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC;
+      const char* kb = reinterpret_cast<const char*>(kc + base);
+      const char* vb = reinterpret_cast<const char*>(vc + base);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) global_to_lds16<PA_DECODE_AUX>(kb + dma_off[c], &ring[wave][SLOT][64 * c]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) global_to_lds16<PA_DECODE_AUX>(vb + dma_off[4 + k], &ring[wave][SLOT][256 + 64 * k]);
+    };
+
+    // Compute window tile n from ring slot SLOT (its loads have landed).
+    auto process = [&](int n, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      constexpr int OFF = SLOT * kSlotBytes;
+      int pos0, lim, phys;
+      tile_span(n, pos0, lim, phys);
+      u32x4 kw[4];
+      u32x2 vt[8];
+      // Rows past the end of the sequence may hold anything (NaN), and a zero
+      // probability times NaN is still NaN: in the tile that holds the end,
+      // each lane zeroes the V rows it fetched that lie past it (in LDS,
+      // before the reads; LDS operations of a wave complete in order).
+      if (pos0 + 16 > lim) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (pos0 + 4 * k + j >= lim) ring[wave][SLOT][256 + 64 * k + lane] = zero;
+      }
+      lds_read_decode_tile<OFF>(kw, vt, k_addr, v_addr);
+      floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[c]), qf[c], st, 0, 0, 0);
+      // st[i]: raw score of token pos0 + 4j + i for column c16.  A tile wholly
+      // inside the visible range (the common case) takes no mask; the others
+      // set their invisible scores to -inf (a wave-uniform branch).
+      const bool full = pos0 >= r.lo && pos0 + 16 <= lim;
+      float s[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = st[i];
+      if (!full) {
+        int d0 = pos0 + 4 * j;
+        asm volatile("" : "+v"(d0));   // keeps the compares out of full tiles
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = (d0 + i < lim && d0 + i >= r.lo) ? s[i] : kNegInf;
+      }
+      float p[4];
+      softmax_step<4>(s, sl2, m, l, oacc, p);
+      const short4v pb = __builtin_bit_cast(short4v, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+#pragma unroll
+      for (int dn = 0; dn < 8; ++dn)
+        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, vt[dn]), pb, oacc[dn], 0,
+                                                              0, 0);
+    };
+    // Ring of NS slots: tile n + NS - 1's loads are issued before tile n is
+    // computed, so NS - 1 tiles are in flight; the wait then lets exactly the
+    // loads issued after tile n stay in flight (none after the last tile, so
+    // no tile is fetched twice).  The compiler cannot count LDS-DMA
+    // completions, so the waits are explicit.  Tiles go round the ring in
+    // groups of NS so that every slot index is a compile-time constant.
+    static_for<0, NS - 1>([&](auto k_c) {
+      if (decltype(k_c)::value < nt) fetch(decltype(k_c)::value, k_c);
+    });
+    for (int n0 = 0; n0 < nt; n0 += NS) {
+      static_for<0, NS>([&](auto k_c) {
+        constexpr int K = decltype(k_c)::value;
+        const int n = n0 + K;
+        if (n < nt) {
+          if (n + NS - 1 < nt) fetch(n + NS - 1, std::integral_constant<int, (K + NS - 1) % NS>{});
+          wait_tiles_ahead<8, NS - 1>(min(NS - 1, nt - 1 - n));
+          process(n, k_c);
+        }
+      });
+    }
+  }
+  finish_unit<G, W>(a, b, g, part, wave, lane, m, l, oacc, 1.f, sm_m, sm_l, sm_acc);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel over E4M3 pools: head_dim 128, block_size a multiple of 16
+// ---------------------------------------------------------------------------
+// Work units and waves as in the bf16 kernel.  The pools hold E4M3 codes
+// (128-byte rows, half the bytes), and a step takes two 16-row tiles, A and B
+// (32 positions):
+//   S^T of each tile: four v_mfma_f32_16x16x32_bf16.  The dot product's dims
+//       run in a permuted order so that MFMA c, lane (j, c16) uses dims
+//       32j + 8c .. +7 (Q is loaded in the same order): a lane's 32 K codes
+//       are one contiguous run, two 16-byte reads, converted to bf16 in
+//       registers.  Lane (j, c16) reads row c16 of tile A and row c16 ^ 8 of
+//       tile B, so the scores a lane ends with are of rows 4j..4j+3 of A and
+//       (4j..4j+3) ^ 8 of B.
+//   online softmax over those eight scores per lane: one max exchange and
+//       one rescale vote per step.
+//   O^T += V^T . P^T: eight v_mfma_f32_16x16x32_bf16, the eight
+//       probabilities of a lane its P^T operand.  V^T comes straight from the
+//       codes: ds_read_b64_tr_b8 hands lane c16 of a 16-lane group byte c16 % 8
+//       of the 8-byte runs that its lanes 2t + c16 / 8 address (t = 0..7), so
+//       lanes 2t and 2t + 1 of group j address dims 16dn .. +15 of the row
+//       behind P^T element t (A's rows for t < 4, B's after) and each lane
+//       converts the 8 codes it receives to bf16.  No bf16 copy of V is made.
+// Ring slot per step (8 KB, NS per wave): K_A, V_A, K_B, V_B, 16 rows x 8
+// chunks each, chunk q of row r at q ^ (r / 2): the K reads of 16 lanes touch
+// every bank once, and so do the transposed reads of each half-wave (16
+// distinct rows, thanks to the ^ 8 for tile B).  The K scale multiplies the
+// softmax scale, the V scale the output.
+template <int G, int BS, int W, int NS>
+__global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_fp8_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int RC8 = D / 16;            // 16-byte chunks per E4M3 row (8)
+  constexpr int TPB = BS / 16;           // 16-row tiles per block
+  constexpr int kTile = 16 * RC8;        // chunks of one tile of one pool (128)
+  constexpr int kSlotBytes = 4 * kTile * 16;
+  __shared__ __attribute__((aligned(16))) u32x4 ring[W][NS][4 * kTile];
+  __shared__ float sm_m[W][G];
+  __shared__ float sm_l[W][G];
+  __shared__ float sm_acc[W > 1 ? W : 1][G][D];
+
+  const UnitId u = unit_id<W>(a);
+  if (u.b < 0) return;
+  const int g = u.g, b = u.b, part = u.part;
+  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4, c16 = lane & 15;
+  const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  const int blk_lo = a.partition_size > 0 ? part * (a.partition_size / BS) : 0;
+
+  // scale handling as in the bf16 kernel, with the K scale folded in
+  const float sl2_raw = a.scale_log2 * a.k_scale[0];
+  const float sl2 = fmaxf(fabsf(sl2_raw), 1.17549435e-38f);
+  const uint32_t qsign = sl2_raw < 0.f ? 0x80008000u : 0u;
+  bf16x8 qf[4];
+  load_group_queries<G, true>(a, b, g, j, c16, qsign, qf);
+  int ids_lo = blk_lo;
+  auto load_ids = [&](int w0) -> int {
+    const int e = ids_lo + wave + W * (w0 + lane);
+    return e < a.max_blocks_per_seq ? table[e] : -1;
+  };
+  int ids = load_ids(0);
+
+  const Range r = work_range(a, b, part);
+  if (r.blk_lo >= r.blk_hi) {
+    if (a.partition_size == 0) store_empty<true, D, G>(a, b, g);
+    return;
+  }
+  if (r.blk_lo != ids_lo) {
+    ids_lo = r.blk_lo;
+    ids = load_ids(0);
+  }
+  {
+    const int lblk = append_block(a, r, wave, W);
+    if (lblk >= 0) {
+      const int phys = table[lblk];
+      if (phys >= 0 && phys < a.num_blocks) append_new_token<D, 2, true>(a, b, g, phys, (r.ctx - 1) % BS, lane);
+    }
+  }
+  const int span = r.blk_hi - r.blk_lo;
+  const int n_blocks = span > wave ? (span - wave + W - 1) / W : 0;
+
+  float m = kNegInf;
+  float l = 0.f;
+  floatx4 oacc[8];     // O^T: dims 16dn + 4j + i of column c16
+#pragma unroll
+  for (int dn = 0; dn < 8; ++dn) oacc[dn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4* kc = static_cast<const u32x4*>(a.k_cache);
+  const u32x4* vc = static_cast<const u32x4*>(a.v_cache);
+
+  // slot-0 LDS addresses of this lane's reads (slot 1: + kSlotBytes).
+  // K: row c16 of tile A, row c16 ^ 8 of tile B; chunks 2j and 2j + 1.
+  uint32_t k_addr[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int rb = c16 ^ 8;
+    k_addr[e] = lds_addr(&ring[wave][0][8 * c16 + ((2 * j + e) ^ (c16 >> 1))]);
+    k_addr[2 + e] = lds_addr(&ring[wave][0][2 * kTile + 8 * rb + ((2 * j + e) ^ (rb >> 1))]);
+  }
+  // V: lane 2t + h of group j addresses the row of P^T element t (A row
+  // 4j + t for t < 4, B row (4j + t - 4) ^ 8 after), dims 16dn + 8h .. +7:
+  // chunk dn of the row, half h.
+  uint32_t v_addr[8];
+  {
+    const int t = c16 >> 1, h = c16 & 1;
+    const int vr = t < 4 ? 4 * j + t : (4 * j + t - 4) ^ 8;
+    const int vbase = t < 4 ? kTile : 3 * kTile;
+#pragma unroll
+    for (int dn = 0; dn < 8; ++dn) v_addr[dn] = lds_addr(&ring[wave][0][vbase + 8 * vr + (dn ^ (vr >> 1))]) + 8 * h;
+  }
+  const float vsc = a.v_scale[0];
+  // LDS-DMA: load i of a tile fills rows 8i + lane / 8; lane % 8 is the stored
+  // chunk position, so the lane fetches source chunk (lane % 8) ^ (row / 2).
+  // Byte offsets from the tile's first row, opaque as in the bf16 kernel.
+  uint32_t dma_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    dma_off[i] = static_cast<uint32_t>((row * RC8 + ((lane & 7) ^ (row >> 1))) * 16);
+    asm volatile("" : "+v"(dma_off[i]));
+  }
+
+  for (int w0 = 0; w0 < n_blocks; w0 += 64) {
+    if (w0 > 0) ids = load_ids(w0);
+    const int wn = min(64, n_blocks - w0);
+    const int nt = wn * TPB;          // tiles of this window
+    const int ns = (nt + 1) >> 1;     // steps; the last holds one tile when nt is odd
+
+    auto tile_span = [&](int n, int& pos0, int& lim, int& phys) {
+      const int i = n / TPB;
+      pos0 = (r.blk_lo + wave + W * (w0 + i)) * BS + (n % TPB) * 16;
+      phys = __builtin_amdgcn_readlane(ids, i);
+      const bool ok = phys >= 0 && phys < a.num_blocks;
+      phys = ok ? phys : 0;
+      lim = ok ? r.ctx : 0;
+    };
+    // Issue the LDS-DMA loads of step s (tiles 2s and, if it exists, 2s + 1;
+    // four loads a tile) into ring slot SLOT.
+    auto fetch = [&](int s, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      static_for<0, 2>([&](auto u_c) {
+        constexpr int U = decltype(u_c)::value;
+        const int n = 2 * s + U;
+        if (U == 0 || n < nt) {
+          int pos0, lim, phys;
+          tile_span(n, pos0, lim, phys);
+          const size_t base = ((static_cast<size_t>(phys) * a.num_kv_heads + g) * BS + (n % TPB) * 16) * RC8;
+          const char* kb = reinterpret_cast<const char*>(kc + base);
+          const char* vb = reinterpret_cast<const char*>(vc + base);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            global_to_lds16<PA_DECODE_AUX>(kb + dma_off[i], &ring[wave][SLOT][2 * U * kTile + 64 * i]);
+            global_to_lds16<PA_DECODE_AUX>(vb + dma_off[i], &ring[wave][SLOT][(2 * U + 1) * kTile + 64 * i]);
+          }
+        }
+      });
+    };
+    // Compute step s from ring slot SLOT (its loads have landed).
+    auto process = [&](int s, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      int pa0, la, pb0 = 0, lb = 0, phys;   // a missing tile B: every row invisible
+      tile_span(2 * s, pa0, la, phys);
+      if (2 * s + 1 < nt) tile_span(2 * s + 1, pb0, lb, phys);
+      // V rows past the end (all of a missing tile B) zeroed before the reads,
+      // as in the bf16 kernel
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (pa0 + 16 > la) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (pa0 + 8 * i + (lane >> 3) >= la) ring[wave][SLOT][kTile + 64 * i + lane] = zero;
+      }
+      if (pb0 + 16 > lb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (pb0 + 8 * i + (lane >> 3) >= lb) ring[wave][SLOT][3 * kTile + 64 * i + lane] = zero;
+      }
+      u32x4 k8[4];
+      u32x2 v8[8];
+      lds_read_fp8_step<SLOT * kSlotBytes>(k8, v8, k_addr, v_addr);
+      floatx4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = c >> 1, w = 2 * (c & 1);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(k8[e][w], k8[e][w + 1])), qf[c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(k8[2 + e][w], k8[2 + e][w + 1])), qf[c], sb, 0, 0, 0);
+      }
+      // sa[i]: raw score of position pa0 + 4j + i, sb[i]: of pb0 + (4j ^ 8) + i
+      const bool full = pa0 >= r.lo && pa0 + 16 <= la && pb0 >= r.lo && pb0 + 16 <= lb;
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = sa[i];
+        sv[4 + i] = sb[i];
+      }
+      if (!full) {
+        int da = pa0 + 4 * j, db = pb0 + ((4 * j) ^ 8);
+        asm volatile("" : "+v"(da), "+v"(db));   // keeps the compares out of full steps
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = (da + i < la && da + i >= r.lo) ? sv[i] : kNegInf;
+          sv[4 + i] = (db + i < lb && db + i >= r.lo) ? sv[4 + i] : kNegInf;
+        }
+      }
+      float p[8];
+      softmax_step<8>(sv, sl2, m, l, oacc, p);
+      const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int dn = 0; dn < 8; ++dn)
+        oacc[dn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(v8[dn][0], v8[dn][1])), pb, oacc[dn], 0, 0, 0);
+    };
+    // Ring of NS slots: step s + NS - 1's loads are issued before step s is
+    // computed, and the wait lets exactly the loads of the steps after s stay
+    // in flight (four per tile; only the window's last step may lack tile B).
+    static_for<0, NS - 1>([&](auto k_c) {
+      if (decltype(k_c)::value < ns) fetch(decltype(k_c)::value, k_c);
+    });
+    for (int s0 = 0; s0 < ns; s0 += NS) {
+      static_for<0, NS>([&](auto k_c) {
+        constexpr int K = decltype(k_c)::value;
+        const int s = s0 + K;
+        if (s < ns) {
+          if (s + NS - 1 < ns) fetch(s + NS - 1, std::integral_constant<int, (K + NS - 1) % NS>{});
+          const int after = min(NS - 1, ns - 1 - s);   // steps issued after s
+          wait_vmcnt_x4<2 * (NS - 1)>(8 * after - (after > 0 && (nt & 1) && s + after == ns - 1 ? 4 : 0));
+          process(s, k_c);
+        }
+      });
+    }
+  }
+  finish_unit<G, W>(a, b, g, part, wave, lane, m, l, oacc, vsc, sm_m, sm_l, sm_acc);
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 namespace {
 
-// LDS ring slots per wave of the split-KV kernel (the single-pass kernel's
-// four waves keep two each).
+// LDS ring slots per wave of the bf16 split-KV kernel (the single-pass
+// kernel's four waves keep two each; the E4M3 kernel has two 32-row slots).
 #ifndef PA_DECODE_SLOTS
 #define PA_DECODE_SLOTS 2
+#endif
+#ifndef PA_DECODE_FP8_SLOTS
+#define PA_DECODE_FP8_SLOTS 2
 #endif
 
 template <int G, int BS, bool KV8>
@@ -789,9 +987,15 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
     const dim3 fg = f.flat_units ? dim3(static_cast<unsigned>(nwg)) : grid;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, KV8, PA_DECODE_SLOTS>), fg, dim3(64), 0, s, f);
-  } else
-    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, KV8, 2>), grid, dim3(256), 0, s, a);
+    if constexpr (KV8)
+      hipLaunchKernelGGL((decode_fp8_kernel<G, BS, 1, PA_DECODE_FP8_SLOTS>), fg, dim3(64), 0, s, f);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 1, PA_DECODE_SLOTS>), fg, dim3(64), 0, s, f);
+  } else if constexpr (KV8) {
+    hipLaunchKernelGGL((decode_fp8_kernel<G, BS, 4, 2>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<G, BS, 4, 2>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -129,6 +129,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n, a multiple of 4 in [0, 4K].
+template <int K>
+__device__ __forceinline__ void wait_vmcnt_x4(int n) {
+  if constexpr (K > 0) {
+    if (n >= 4 * K) {
+      wait_vmcnt<4 * K>();
+      return;
+    }
+    wait_vmcnt_x4<K - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // f(std::integral_constant<int, k>) for k = K .. N-1, unrolled (compile-time
 // indices, e.g. of LDS ring slots).
 template <int K, int N, class F>

@@ -194,7 +194,9 @@ def main(argv=None):
     ap.add_argument("--partition-size", type=int, default=1024,
                     help="split-KV partition of the headline decode step (the fastest of those timed in "
                          "roofline.partition_size_variants on MI355X)")
-    ap.add_argument("--fp8-partition-size", type=int, default=256)
+    ap.add_argument("--fp8-partition-size", type=int, default=512,
+                    help="split-KV partition of the E4M3 decode (256 and 512 within 1%% on MI355X; 512 leaves "
+                         "the merge half the partials)")
     ap.add_argument("--copies", type=int, default=3, help="independent input copies rotated per step")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")

@@ -16,7 +16,7 @@ from attention_paged_kv_write_amd import build
 
 HOT = {
     "prefill.hip": ("prefill_mfma_kernel",),
-    "decode.hip": ("decode_mfma_kernel", "decode_generic_kernel"),
+    "decode.hip": ("decode_mfma_kernel", "decode_fp8_kernel", "decode_generic_kernel"),
     "reduce.hip": ("reduce_kernel", "reduce_small_kernel"),
     "kv_write.hip": ("",),
     "rope.hip": ("rope_kv_write_kernel",),
