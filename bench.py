@@ -204,6 +204,7 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache figures")
     ap.add_argument("--no-c4", action="store_true", help="skip the Llama-2-70B prefix-sharing decode figures")
     ap.add_argument("--no-c5", action="store_true", help="skip the long-context split-KV decode figures")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured step timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -340,8 +341,10 @@ def main(argv=None):
     # Both steps again with their launches captured in a HIP graph (one capture
     # holds one step per input copy), so the figure is GPU time, not Python.
     graph_reps = max(1, args.steps // len(copies))
-    g2 = graph_ms(torch, stream, lambda i: step(copies[i]), len(copies), graph_reps)
-    g3 = graph_ms(torch, stream, lambda i: step_separate(copies[i]), len(copies), graph_reps)
+    g2 = g3 = None
+    if not args.no_graph:
+        g2 = graph_ms(torch, stream, lambda i: step(copies[i]), len(copies), graph_reps)
+        g3 = graph_ms(torch, stream, lambda i: step_separate(copies[i]), len(copies), graph_reps)
     log(f"graph-captured step: {g2 * 1e3 if g2 else float('nan'):.1f} us (two launches), "
         f"{g3 * 1e3 if g3 else float('nan'):.1f} us (three launches)")
 
