@@ -4,19 +4,28 @@ One step = the decode hot path on the Llama-3-8B-shaped workload (64
 sequences, 32 query / 8 KV heads, head_dim 128, 16-token blocks, contexts
 uniform in [128, 2048], shuffled pool 1.25x the need): the cache write of the
 64 new tokens folded into the split-KV decode (paged_attention_decode_append,
-256-token partitions), then paged_attention_reduce; the same step as three
-launches (paged_kv_write first) is timed beside it.  The headline value is KV-cache bytes streamed per
-second (sum of context lengths x 8 KV heads x (K + V) x 128 x 2 bytes per step).
+1024-token partitions), then paged_attention_reduce.  The headline value is
+KV-cache bytes streamed per second (sum of context lengths x 8 KV heads x
+(K + V) x 128 x 2 bytes per step).  Beside it: the same step as three
+launches (paged_kv_write first), both steps captured in a HIP graph, the
+decode kernel alone at other partition sizes, and the paged stream probe
+(paged_kv_stream_read: the same units and tiles read with no attention, the
+ceiling of decode's access pattern) with torch's copy and sum.
 
-Inputs are resident in HBM before timing.  R independent copies of the pools,
+Inputs are resident in HBM before timing.  Independent copies of the pools,
 tables and queries are rotated so the 256 MB Infinity Cache cannot serve one
-step's KV from the previous step.  The varlen causal prefill on the
-Llama-3-8B varlen workload (16 sequences, lengths uniform in [64, 2048]) is
-timed as a secondary figure (TFLOP/s over unmasked query-key pairs), and so
-are the chunked paged prefill (16 sequences, cached prefix 0..3072, chunk
-128..1024) and, under a 2048-key sliding window, the split decode of 64
-sequences of 1024..16384 positions (GB/s over the window's KV bytes) and the
-chunked paged prefill (TFLOP/s over the window's query-key pairs).
+step's KV from the previous step.  Secondary figures, each with its own
+roofline: the varlen causal prefill on the Llama-3-8B varlen workload (16
+sequences, lengths uniform in [64, 2048]; TFLOP/s over unmasked query-key
+pairs), the prompt cache write and the fused RoPE cache write of its rows,
+the chunked paged prefill (16 sequences, cached prefix 0..3072, chunk
+128..1024); under a 2048-key sliding window, the split decode of 64 sequences
+of 1024..16384 positions (GB/s over the window's KV bytes) and the chunked
+paged prefill; the decode over an E4M3 cache (512-token partitions) and its
+history write; the Llama-2-70B prefix-shared decode (256 sequences, GB/s over
+unique KV bytes) and the long-context split decode (4 x 131072 positions).
+The fp64 oracle is timed on the host cores beside the decode, the prefill and
+the two large decode workloads.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
