@@ -166,6 +166,7 @@ int decode_call(const char* fn, void* out, float* lse, float* part_out, float* p
   a.v_scale = kv8 ? v_scale : nullptr;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.pack_shared = 0;   // the launcher decides
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (kv8) {

@@ -397,20 +397,64 @@ __device__ __forceinline__ UnitId unit_id(const DecodeArgs& a) {
   return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
 }
 
+// Column packing.  The 16 B-operand columns of the matrix products hold the G
+// query heads of one sequence; with G < 16 the other columns can carry the
+// heads of PK - 1 = 16/G - 1 more sequences at no extra matrix work, when
+// they read the same keys.  Sequences L = b - b % PK .. L + PK - 1 form a
+// pack: member L + k joins its leader's work unit for a partition when both
+// see the whole partition and their block ids over it are identical (the
+// blocks of a prompt shared copy-on-write, "PageAttention + FlashAttention
+// golden combination", section 2.1).  The leader's unit then computes the
+// partition for every member (column c16 belongs to member c16 / G) and the
+// members' own units exit; a sequence that shares nothing with its leader is
+// its own unit as before.  Both sides take the decision from the same table
+// entries and context lengths, so it is the same on both.
+struct Pack {
+  int lead;          // the sequence whose unit computes this partition
+  uint32_t mask;     // bit k: sequence lead + k is in the unit
+  bool follower;     // this unit's partition is computed by its leader's unit
+};
+template <int PK, int BS>
+__device__ __forceinline__ Pack pack_of(const DecodeArgs& a, int b, int part, int lane) {
+  const int nblk = a.partition_size / BS;   // at most 64 (checked by the launcher)
+  const int e = part * nblk + lane;
+  const bool in = lane < nblk && e < a.max_blocks_per_seq;
+  const int cap = min(a.max_context_len, a.max_blocks_per_seq * BS);
+  const int pend = (part + 1) * a.partition_size;
+  const int lead = b - b % PK;
+  auto row = [&](int s) { return a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq; };
+  auto whole = [&](int s) { return clampi(a.context_lens[s], 0, cap) >= pend; };
+  const int lead_id = in ? row(lead)[e] : 0;
+  const bool lead_whole = whole(lead);
+  auto shares = [&](int s) {
+    const int id = in ? row(s)[e] : 0;
+    return lead_whole && whole(s) && __builtin_amdgcn_ballot_w64(id != lead_id) == 0;
+  };
+  if (b != lead) return Pack{b, 1u, shares(b)};
+  uint32_t mask = 1u;
+#pragma unroll
+  for (int k = 1; k < PK; ++k)
+    if (lead + k < a.num_seqs && shares(lead + k)) mask |= 1u << k;
+  return Pack{lead, mask, false};
+}
+
 // The group's queries as the B operand of the four QK^T MFMAs: column c16 is
-// query head g*G + c16 (zero past G); MFMA c takes 16-byte chunk 4c + j of
-// the bf16 row, or chunk 4j + c when the dims run in the E4M3 kernel's
-// permuted order.  qsign flips the sign bits (a negative softmax scale).
+// query head g*G + c16 % G of sequence b + c16 / G when bit c16 / G of pack is
+// set, else zero; MFMA c takes 16-byte chunk 4c + j of the bf16 row, or chunk
+// 4j + c when the dims run in the E4M3 kernel's permuted order.  qsign flips
+// the sign bits (a negative softmax scale).
 template <int G, bool PERMUTED>
-__device__ __forceinline__ void load_group_queries(const DecodeArgs& a, int b, int g, int j, int c16,
-                                                   uint32_t qsign, bf16x8* qf) {
+__device__ __forceinline__ void load_group_queries(const DecodeArgs& a, int b, uint32_t pack, int g, int j,
+                                                   int c16, uint32_t qsign, bf16x8* qf) {
   constexpr int RC = 16;   // 16-byte chunks per bf16 row of 128
   const u32x4* qc = static_cast<const u32x4*>(a.q);
-  const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
+  const int k = c16 / G;
+  const bool live = k < 32 && ((pack >> k) & 1u);
+  const size_t row = static_cast<size_t>(b + k) * a.num_q_heads + g * G + c16 % G;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (c16 < G) w = qc[row * RC + (PERMUTED ? 4 * j + c : 4 * c + j)] ^ qsign;
+    if (live) w = qc[row * RC + (PERMUTED ? 4 * j + c : 4 * c + j)] ^ qsign;
     qf[c] = __builtin_bit_cast(bf16x8, w);
   }
 }
@@ -419,18 +463,21 @@ __device__ __forceinline__ void load_group_queries(const DecodeArgs& a, int b, i
 // 16-lane rows, then O / l (times vsc, the V scale of an E4M3 pool) and the
 // log-sum-exp stored as the unit's partial result (split mode), or as the
 // final result (single pass: W == 1) or merged across the W waves in LDS first.
+// W == 1: column c16 is head g*G + c16 % G of sequence b + c16 / G, stored when
+// bit c16 / G of pack is set.
 template <int G, int W>
-__device__ __forceinline__ void finish_unit(const DecodeArgs& a, int b, int g, int part, int wave, int lane,
-                                            float m, float l, const floatx4* oacc, float vsc,
+__device__ __forceinline__ void finish_unit(const DecodeArgs& a, int b, uint32_t pack, int g, int part,
+                                            int wave, int lane, float m, float l, const floatx4* oacc, float vsc,
                                             float (*sm_m)[G], float (*sm_l)[G], float (*sm_acc)[G][128]) {
   constexpr int D = 128;
   const int j = lane >> 4, c16 = lane & 15;
   l = across_rows(l, OpSum());
   if constexpr (W == 1) {
-    if (c16 >= G) return;
+    const int k = c16 / G;
+    if (k >= 32 || !((pack >> k) & 1u)) return;
     const float inv = vsc / l;
     const float lse = (m + __log2f(l)) * kLn2;
-    const size_t row = static_cast<size_t>(b) * a.num_q_heads + g * G + c16;
+    const size_t row = static_cast<size_t>(b + k) * a.num_q_heads + g * G + c16 % G;
     if (a.partition_size > 0) {
       const size_t pr = row * a.num_partitions + part;
 #pragma unroll
@@ -538,10 +585,21 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
 
   const UnitId u = unit_id<W>(a);
   if (u.b < 0) return;
-  const int g = u.g, b = u.b, part = u.part;
+  const int g = u.g, part = u.part;
   const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 4, c16 = lane & 15;
+  // split mode: sequences sharing this partition's blocks go in one unit
+  int b = u.b;
+  uint32_t pack = 1u;
+  if constexpr (W == 1 && G < 16) {
+    if (a.pack_shared) {
+      const Pack pk = pack_of<16 / G, BS>(a, b, part, lane);
+      if (pk.follower) return;
+      b = __builtin_amdgcn_readfirstlane(pk.lead);
+      pack = __builtin_amdgcn_readfirstlane(pk.mask);
+    }
+  }
   const int32_t* table = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
   const int blk_lo = a.partition_size > 0 ? part * (a.partition_size / BS) : 0;
 
@@ -554,7 +612,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
   const float sl2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   bf16x8 qf[4];
-  load_group_queries<G, false>(a, b, g, j, c16, qsign, qf);
+  load_group_queries<G, false>(a, b, pack, g, j, c16, qsign, qf);
   int ids_lo = blk_lo;   // first block of the id window; moves up under a window
   auto load_ids = [&](int w0) -> int {
     const int e = ids_lo + wave + W * (w0 + lane);
@@ -719,7 +777,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_mfma_kernel(Dec
       });
     }
   }
-  finish_unit<G, W>(a, b, g, part, wave, lane, m, l, oacc, 1.f, sm_m, sm_l, sm_acc);
+  finish_unit<G, W>(a, b, pack, g, part, wave, lane, m, l, oacc, 1.f, sm_m, sm_l, sm_acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -775,7 +833,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_fp8_kernel(Deco
   const float sl2 = fmaxf(fabsf(sl2_raw), 1.17549435e-38f);
   const uint32_t qsign = sl2_raw < 0.f ? 0x80008000u : 0u;
   bf16x8 qf[4];
-  load_group_queries<G, true>(a, b, g, j, c16, qsign, qf);
+  load_group_queries<G, true>(a, b, 1u, g, j, c16, qsign, qf);
   int ids_lo = blk_lo;
   auto load_ids = [&](int w0) -> int {
     const int e = ids_lo + wave + W * (w0 + lane);
@@ -955,7 +1013,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_fp8_kernel(Deco
       });
     }
   }
-  finish_unit<G, W>(a, b, g, part, wave, lane, m, l, oacc, vsc, sm_m, sm_l, sm_acc);
+  finish_unit<G, W>(a, b, 1u, g, part, wave, lane, m, l, oacc, vsc, sm_m, sm_l, sm_acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -986,6 +1044,9 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
       per_seq = (a.window - 1) / a.partition_size + 2;
     const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
+    // column packing needs a partition's block ids in one load per lane, and
+    // leaves out the window and the append (whose rows differ per sequence)
+    f.pack_shared = !KV8 && G < 16 && a.window == 0 && a.k_new == nullptr && a.partition_size / BS <= 64;
     const dim3 fg = f.flat_units ? dim3(static_cast<unsigned>(nwg)) : grid;
     if constexpr (KV8)
       hipLaunchKernelGGL((decode_fp8_kernel<G, BS, 1, PA_DECODE_FP8_SLOTS>), fg, dim3(64), 0, s, f);

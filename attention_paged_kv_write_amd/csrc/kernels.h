@@ -85,6 +85,7 @@ struct DecodeArgs {
   const float* v_scale;
   const void* k_new;     // append: [B, H_kv, d] K/V of the token at position ctx-1 (T),
   const void* v_new;     //   stored into the pool by the kernel before it is read; else null
+  int pack_shared;       // split bf16 MFMA kernel: pack sequences that share a partition's blocks
 };
 
 struct ReduceArgs {

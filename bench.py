@@ -341,6 +341,7 @@ def main(argv=None):
                 "traffic": traffic,
                 "kernel": "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode)",
                 "kernel_avg_us": round(dec_avg_ms * 1e3, 2),
+                "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
                 "kernel_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                 "kernel_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                 "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
@@ -510,6 +511,7 @@ def main(argv=None):
         log(f"fused rope + kv write {rms * 1e3:.1f} us -> {rgbs:.0f} GB/s")
         prefill = {"workload": pc.spec.name, "total_tokens": pc.total_tokens,
                    "kernel_avg_us": round(pms * 1e3, 1), "tflops": round(tflops, 1),
+                   "kernel_median_us": round(float(np.median(p_ms)) * 1e3, 1),
                    "kernel_p10_us": round(float(np.percentile(p_ms, 10)) * 1e3, 1),
                    "kernel_p90_us": round(float(np.percentile(p_ms, 90)) * 1e3, 1),
                    "input_copies": 2,
@@ -828,6 +830,7 @@ def main(argv=None):
                             "frac": round(ugbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(traffic_file, DECODE_SOURCES),
                             "kernel": kernel_name, "kernel_avg_us": round(davg * 1e3, 2),
+                            "kernel_median_us": round(float(np.median(dms)) * 1e3, 2),
                             "kernel_p10_us": round(float(np.percentile(dms, 10)) * 1e3, 2),
                             "kernel_p90_us": round(float(np.percentile(dms, 90)) * 1e3, 2),
                             "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",

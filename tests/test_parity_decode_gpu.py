@@ -208,6 +208,67 @@ def test_decode_matches_oracle(name):
         assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"{name} partition_size={ps}")
 
 
+# Sequences whose block ids agree over a whole partition (a shared prompt) ride
+# in one split work unit, the 16 MFMA columns holding 16 / G sequences' heads.
+# Groups aligned with the packs, groups that straddle them (3 per group with
+# packs of 4), partitions inside, across and past the shared blocks.
+SHARED_CASES = {
+    "g8_pairs_bs32": (4, dict(batch=16, ctx_min=512, ctx_max=1400, max_blocks_per_seq=44), (512, 256, 0)),
+    "g4_quads": (2, dict(batch=8, share_group=4, share_blocks=32, ctx_min=520, ctx_max=1200,
+                         max_blocks_per_seq=75), (256, 512, 768)),
+    "g4_groups_of_3": (2, dict(batch=12, share_group=3, share_blocks=20, ctx_min=330, ctx_max=900,
+                               max_blocks_per_seq=57), (64, 160, 320)),
+    "g2_octets": (2, dict(batch=16, num_q_heads=8, num_kv_heads=4, share_group=8, share_blocks=8,
+                          ctx_min=130, ctx_max=600, max_blocks_per_seq=38), (64, 128)),
+    "g1_sixteen": (2, dict(batch=32, num_q_heads=4, num_kv_heads=4, share_group=16, share_blocks=4,
+                           ctx_min=70, ctx_max=300, max_blocks_per_seq=19), (32, 64)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHARED_CASES))
+def test_shared_blocks_packed_match_oracle(name):
+    cfg, over, psizes = SHARED_CASES[name]
+    case = wl.make_case(cfg, **over)
+    ref_out, ref_lse, _, _ = oracle_decode(case)
+    for ps in psizes:
+        out, lse, _, _, _ = run_decode(case, ps)
+        assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"{name} partition_size={ps}")
+
+
+@pytest.mark.parametrize("name", ["g4_quads", "g8_pairs_bs32"])
+def test_shared_blocks_packed_growing_scores(name):
+    # keys grow along u with the position and each sequence's queries lie along
+    # u with its own length, so the columns of one packed unit see their maxima
+    # grow at different rates and every column's running max moves when any
+    # column's does
+    cfg, over, psizes = SHARED_CASES[name]
+    case = wl.make_case(cfg, **over)
+    rng = np.random.default_rng(16)
+    sp = case.spec
+    bs, d = sp.block_size, sp.head_dim
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    kc = wl.bf16_bits_to_f32(case.k_cache).astype(np.float64)
+    hist = case.context_lens.astype(np.int64) - (1 if sp.write_new_token else 0)
+    for b in range(sp.batch):
+        for p in range(int(hist[b])):
+            blk = int(case.block_tables[b, p // bs])
+            kc[blk, :, p % bs, :] = 0.3 * p * u + 0.01 * np.sin(p + np.arange(d))
+    case.k_cache = wl.f32_to_bf16_bits(np.nan_to_num(kc).astype(np.float32))
+    case.k_cache[np.isnan(kc)] = wl.BF16_NAN
+    if sp.write_new_token:
+        last = (case.context_lens.astype(np.int64) - 1).astype(np.float64)
+        case.k_new = wl.f32_to_bf16_bits((0.3 * last[:, None, None] * u[None, None, :]).astype(np.float32)
+                                         + np.zeros(case.k_new.shape, np.float32))
+    mag = 1.0 + 1.5 * (np.arange(sp.batch) % 4)
+    case.q = wl.f32_to_bf16_bits((mag[:, None, None] * u[None, None, :]
+                                  + 0.01 * rng.standard_normal(case.q.shape)).astype(np.float32))
+    ref_out, ref_lse, _, _ = oracle_decode(case)
+    for ps in psizes:
+        out, lse, _, _, _ = run_decode(case, ps)
+        assert_parity(out, lse, ref_out, ref_lse, sp.dtype, f"{name} growing partition_size={ps}")
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_full", "bf16_g8_bs16_ctx1", "bf16_g1_bs32"])
 def test_vector_kernel_matches_mfma_kernel(name):
     cfg, over, psizes = DECODE_CASES[name]
