@@ -787,7 +787,7 @@ def main(argv=None):
         xB, xHq, xHkv, xd, xbs, xps = (xs.batch, xs.num_q_heads, xs.num_kv_heads, xs.head_dim, xs.block_size,
                                        xs.partition_size)
         xmax = xc.max_context_len
-        xP = ops.num_partitions(xmax, xps)
+        xP = ops.num_partitions(xmax, xps) if xps else 1
         ctx64 = xc.context_lens.astype(np.int64)
         logical = int(ctx64.sum()) * xHkv * 2 * xd * 2
         if xs.share_group:
@@ -804,20 +804,36 @@ def main(argv=None):
                                 out=torch.empty((xB, xHq, xd), dtype=torch.bfloat16, device=dev),
                                 lse=torch.empty((xB, xHq), dtype=torch.float32, device=dev)))
 
-        def xdecode(i):
+        def xdecode(i, ps=xps):
             c = xcopies[i]
-            ops.paged_attention_decode(c["q"], c["kc"], c["vc"], bt, cl, xmax, xc.scale, xps,
-                                       part_out=c["po"], part_lse=c["pl"])
+            if ps:
+                ops.paged_attention_decode(c["q"], c["kc"], c["vc"], bt, cl, xmax, xc.scale, ps,
+                                           part_out=c["po"], part_lse=c["pl"])
+            else:
+                ops.paged_attention_decode(c["q"], c["kc"], c["vc"], bt, cl, xmax, xc.scale,
+                                           out=c["out"], lse=c["lse"])
 
         def xstep(i):
             xdecode(i)
-            c = xcopies[i]
-            ops.paged_attention_reduce(c["po"], c["pl"], cl, xps, out=c["out"], lse=c["lse"])
+            if xps:
+                c = xcopies[i]
+                ops.paged_attention_reduce(c["po"], c["pl"], cl, xps, out=c["out"], lse=c["lse"])
         for i in range(4):
             xstep(i % n_copies)
         ng = max(2, args.steps // 40)
         dms = timed_groups(torch, stream, xdecode, n_copies, ng)
         sms = timed_groups(torch, stream, xstep, n_copies, ng)
+        # a one-pass workload: the split kernel at 512-token partitions beside it
+        split = {}
+        if not xps:
+            sP = ops.num_partitions(xmax, 512)
+            for c in xcopies:
+                c["po"] = torch.empty((xB, xHq, sP, xd), dtype=torch.float32, device=dev)
+                c["pl"] = torch.empty((xB, xHq, sP), dtype=torch.float32, device=dev)
+            xdecode(0, 512)
+            vms = timed_groups(torch, stream, lambda i: xdecode(i, 512), n_copies, ng)
+            split = {"512": {"kernel_avg_us": round(float(np.mean(vms)) * 1e3, 2),
+                             "gbs_unique": round(unique / (float(np.mean(vms)) * 1e-3) / 1e9, 1)}}
         davg, savg = float(np.mean(dms)), float(np.mean(sms))
         ugbs = unique / (davg * 1e-3) / 1e9
         res = {"workload": xs.name, "batch": xB, "num_q_heads": xHq, "num_kv_heads": xHkv, "block_size": xbs,
@@ -835,6 +851,8 @@ def main(argv=None):
                             "kernel_p90_us": round(float(np.percentile(dms, 90)) * 1e3, 2),
                             "timing": "HIP events on the launch stream around groups of 10 back-to-back launches",
                             "algorithmic_bytes_per_launch": unique}}
+        if split:
+            res["roofline"]["partition_size_variants"] = split
         log(f"workload {cfg}: decode kernel {davg * 1e3:.1f} us -> {ugbs:.0f} GB/s unique "
             f"({logical / (davg * 1e-3) / 1e9:.0f} logical); step {savg * 1e3:.1f} us")
         del xcopies, bt, cl
@@ -846,7 +864,7 @@ def main(argv=None):
 
     # the pools of one copy (2.5-2.7 GB) exceed the Infinity Cache many times over
     c4 = None if args.no_c4 else decode_workload(
-        4, 2, C4_TRAFFIC_FILE, "decode_mfma_kernel<G=8,BS=32,W=1> (paged_attention_decode)")
+        4, 2, C4_TRAFFIC_FILE, "decode_mfma_kernel<G=8,BS=32,W=4> (paged_attention_decode, one pass)")
     c5 = None if args.no_c5 else decode_workload(
         5, 1, C5_TRAFFIC_FILE, "decode_mfma_kernel<G=4,BS=16,W=1> (paged_attention_decode) + reduce_kernel")
 

@@ -389,13 +389,17 @@ def oracle_decode_by_sequence(case):
 @pytest.mark.parametrize("cfg", [4, 5])
 def test_full_size_every_output(cfg):
     # workload 4 (256 sequences, 64 heads in groups of 8, shared 512-token
-    # prefixes, 32-token blocks) and workload 5 (4 x 131072 positions, 256
-    # partitions of 512 merged by the general reduce): all outputs compared
+    # prefixes, 32-token blocks: one pass as the bench runs it, and split at
+    # 512, where pairs of sequences share their first partition's unit) and
+    # workload 5 (4 x 131072 positions, 256 partitions of 512 merged by the
+    # general reduce): all outputs compared
     case = wl.make_case(cfg)
     assert not case.spec.write_new_token
-    out, lse, _, _, _ = run_decode(case, case.spec.partition_size)
     ref_out, ref_lse = oracle_decode_by_sequence(case)
-    assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype, f"workload {cfg}, every (sequence, head)")
+    for ps in ((case.spec.partition_size, 512) if cfg == 4 else (case.spec.partition_size,)):
+        out, lse, _, _, _ = run_decode(case, ps)
+        assert_parity(out, lse, ref_out, ref_lse, case.spec.dtype,
+                      f"workload {cfg} partition_size={ps}, every (sequence, head)")
 
 
 def test_needle_many_partitions_bit_exact():
