@@ -135,6 +135,9 @@ int paged_kv_write(const void* k, const void* v, void* k_cache, void* v_cache,
  *   paged_attention_reduce merges the partitions.  partition_size must be a
  *   multiple of block_size.  The partition dimension of part_out/part_lse is
  *   max_partitions = ceil(max_context_len / partition_size).
+ *   Sequences whose block ids agree over a whole partition (blocks of a shared
+ *   prompt) may be computed in one work unit; their results are the same up to
+ *   rounding, and identical for any permutation of the pool's blocks.
  *   q             [B, H_q, head_dim], dtype
  *   block_tables  int32 [B, max_blocks_per_seq]
  *   context_lens  int32 [B]; each <= max_context_len
