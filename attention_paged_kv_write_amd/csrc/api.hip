@@ -42,7 +42,6 @@ int launch_status(hipError_t e, const char* what) {
 
 bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
 int esize(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
-bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 // Partition dimension of a split decode's partials.
 int split_parts(int max_context_len, int partition_size) {

@@ -330,6 +330,8 @@ __device__ __forceinline__ void lds_read_decode_tile(u32x4* kw, u32x2* vt, const
         "v"(v_addr[2]), "v"(v_addr[3]), "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7]),
         "i"(OFF)
       : "memory");
+#else
+  (void)kw; (void)vt; (void)k_addr; (void)v_addr;
 #endif
 }
 
@@ -360,6 +362,8 @@ __device__ __forceinline__ void lds_read_fp8_step(u32x4* k8, u32x2* v8, const ui
         "v"(v_addr[2]), "v"(v_addr[3]), "v"(v_addr[4]), "v"(v_addr[5]), "v"(v_addr[6]), "v"(v_addr[7]),
         "i"(OFF)
       : "memory");
+#else
+  (void)k8; (void)v8; (void)k_addr; (void)v_addr;
 #endif
 }
 

@@ -40,6 +40,8 @@ __device__ __forceinline__ void lds_read_slot8(u32x4* w, uint32_t addr) {
         "=&v"(w[7])
       : "v"(addr)
       : "memory");
+#else
+  (void)w; (void)addr;
 #endif
 }
 
