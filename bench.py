@@ -27,7 +27,7 @@ unique KV bytes) and the long-context split decode (4 x 131072 positions).
 The fp64 oracle is timed on the host cores beside the decode, the prefill and
 the two large decode workloads.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -221,7 +221,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
