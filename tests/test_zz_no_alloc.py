@@ -49,6 +49,34 @@ def test_noalloc_matches_split_decode_twice(window):
         assert_parity(to_host_f64(out), to_host_f64(lse), o_out, o_lse, case.spec.dtype, f"noalloc ps={ps}")
 
 
+@pytest.mark.gpu
+def test_noalloc_in_a_hip_graph():
+    # the call as its callers make it under graph capture: captured once, then
+    # replayed three times with eager work (refilling the outputs with NaN)
+    # between the replays; every replay equals the two-call path bit for bit
+    case = wl.make_case(2, seed=91, batch=12, ctx_min=1, ctx_max=1500, max_blocks_per_seq=94)
+    ps = 256
+    (q, kc, vc, bt, cl), ref_out, ref_lse = _reference(case, ps, 0)
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    # an eager call first, so the scratch address is looked up outside the capture
+    ops.paged_attention_decode_noalloc(q, kc, vc, bt, cl, case.max_context_len, case.scale, ps, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.paged_attention_decode_noalloc(q, kc, vc, bt, cl, case.max_context_len, case.scale, ps, out, lse)
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), r
+        assert torch.equal(lse, ref_lse), r
+    del g
+
+
 def test_noalloc_refuses_partials_past_the_scratch():
     # 4 sequences x 32 heads x 2048 partitions x 129 floats = 135 MB > 32 MiB:
     # refused by the host checks, nothing launched (no GPU needed)
