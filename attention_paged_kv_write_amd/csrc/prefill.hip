@@ -297,14 +297,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       }
     }
     bf16x8 pf[2][RG];   // P^T B operands: [key chunk of 32][rg]
+    // Raw scores: the scale (positive here) is applied after the max,
+    // max(s) * scale == max(s * scale) exactly, and inside the exponent's FMA.
+    // The maxima are IEEE maximum (v_maximum3_f32), which the compiler builds
+    // without NaN-quieting copies and whose reads of the matrix-core results it
+    // orders itself.
+    float sv[RG][4][4], lmx[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      // Raw scores: the scale (positive here) is applied after the max,
-      // max(s) * scale == max(s * scale) exactly, and inside the exponent's
-      // FMA.  The max is IEEE maximum (v_maximum3_f32), which the compiler
-      // builds without NaN-quieting copies and whose reads of the matrix-core
-      // results it orders itself.
-      float sv[4][4];
       // The row's position (among the keys) minus this lane's first key of the
       // tile, kt*64 + 4j: key kt*64 + 4j + 16nt + i is visible iff
       // 0 <= d - (16nt + i) < wlim, one unsigned compare per element.
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[nt][i] = sacc[nt][rg][i];
+        for (int i = 0; i < 4; ++i) sv[rg][nt][i] = sacc[nt][rg][i];
       if (masked) {
         // (opaque, so that the compares are not hoisted into unmasked tiles)
         int dm = d;
@@ -321,27 +321,40 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (static_cast<unsigned>(dm - (16 * nt + i)) >= wlim) sv[nt][i] = kNegInf;
+            if (static_cast<unsigned>(dm - (16 * nt + i)) >= wlim) sv[rg][nt][i] = kNegInf;
       }
       auto mx2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
-      float mx = mx2(mx2(mx2(mx2(sv[0][0], sv[0][1]), mx2(sv[0][2], sv[0][3])),
-                         mx2(mx2(sv[1][0], sv[1][1]), mx2(sv[1][2], sv[1][3]))),
-                     mx2(mx2(mx2(sv[2][0], sv[2][1]), mx2(sv[2][2], sv[2][3])),
-                         mx2(mx2(sv[3][0], sv[3][1]), mx2(sv[3][2], sv[3][3]))));
-      mx = quarter_max(mx) * sl2;
-      // lazy rescale: the whole wave moves its maxima only when some row's
-      // max has grown past the slack.  A row with no visible key in a masked
-      // tile has mx = -inf and keeps its m, which stays -inf until the row's
-      // first visible key (possible only under a sliding window).
-      const uint64_t grow = __builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack);
-      if (grow) {
-        const float m_new = fmaxf(m[rg], mx);
-        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m[rg] - m_new);
-        m[rg] = m_new;
-        l[rg] *= alpha;
+      const float(&v)[4][4] = sv[rg];
+      lmx[rg] = mx2(mx2(mx2(mx2(v[0][0], v[0][1]), mx2(v[0][2], v[0][3])),
+                        mx2(mx2(v[1][0], v[1][1]), mx2(v[1][2], v[1][3]))),
+                    mx2(mx2(mx2(v[2][0], v[2][1]), mx2(v[2][2], v[2][3])),
+                        mx2(mx2(v[3][0], v[3][1]), mx2(v[3][2], v[3][3]))));
+    }
+    // Lazy rescale: a row moves its maximum only when its tile max has grown
+    // past the slack.  Some row's max exceeds its m + slack exactly when some
+    // lane's own max does (the four lanes of a row hold the same m), so one
+    // ballot of lane maxima over both row groups decides, and the row maxima
+    // (across the four key quarters) are formed only on that rare path.  A row
+    // with no visible key in a masked tile has max -inf and keeps its m, which
+    // stays -inf until the row's first visible key (possible only under a
+    // sliding window).
+    if (__builtin_amdgcn_ballot_w64((lmx[0] * sl2 > m[0] + kRescaleSlack) |
+                                   (lmx[1] * sl2 > m[1] + kRescaleSlack))) {
 #pragma unroll
-        for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
+      for (int rg = 0; rg < RG; ++rg) {
+        const float mx = quarter_max(lmx[rg]) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > m[rg] + kRescaleSlack)) {
+          const float m_new = fmaxf(m[rg], mx);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m[rg] - m_new);
+          m[rg] = m_new;
+          l[rg] *= alpha;
+#pragma unroll
+          for (int dn = 0; dn < 8; ++dn) oacc[rg][dn] *= alpha;
+        }
       }
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
       const float ms = m[rg] == kNegInf ? 0.f : m[rg];
       uint32_t pw[4][2];
       float ps[4];
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
       for (int nt = 0; nt < 4; ++nt) {
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(fmaf(sv[nt][i], sl2, -ms));   // masked: exp2(-inf) = 0
+        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(fmaf(sv[rg][nt][i], sl2, -ms));   // masked: exp2(-inf) = 0
         ps[nt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pw[nt][0] = pack_bf16x2(pv[0], pv[1]);
         pw[nt][1] = pack_bf16x2(pv[2], pv[3]);
