@@ -390,13 +390,28 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 struct UnitId {
   int g, b, part;
 };
-template <int W>
+// Flat grid ids: head-major (id = unit * H_kv + g) puts KV head g of every
+// unit on XCD id mod 8; XCD-major (XM) gives XCD x the units u = x mod 8 with
+// all their KV heads (id = (u / 8) * 8 H_kv + g * 8 + u mod 8, the grid
+// rounded up to a multiple of 8 H_kv), so an XCD reads every head's slab of
+// the blocks it touches.  The E4M3 kernel, whose 2 KB slabs are half the
+// bf16 ones, streams a little faster XCD-major (workload 8 at 512-token
+// partitions, same-box A/B on three boxes: 1.4-3.8%, e.g. 28.34 +- 0.13 vs
+// 28.74 +- 0.10 us over four rounds); the bf16 kernel at its 1024-token
+// partitions does not (48.0-48.2 vs 47.8-47.9 us), so it stays head-major.
+template <int W, bool XM = false>
 __device__ __forceinline__ UnitId unit_id(const DecodeArgs& a) {
   if (W == 1 && a.flat_units) {
-    const Unit un = flat_unit(a, blockIdx.x / a.num_kv_heads);
+    const int Hkv = a.num_kv_heads;
+    int ui = blockIdx.x / Hkv, gi = blockIdx.x % Hkv;
+    if constexpr (XM) {
+      const int r = blockIdx.x >> 3;
+      gi = r % Hkv;
+      ui = (r / Hkv) * 8 + (blockIdx.x & 7);
+    }
+    const Unit un = flat_unit(a, ui);
     if (un.b < 0) return {0, -1, 0};
-    return {static_cast<int>(blockIdx.x % a.num_kv_heads), __builtin_amdgcn_readfirstlane(un.b),
-            __builtin_amdgcn_readfirstlane(un.part)};
+    return {gi, __builtin_amdgcn_readfirstlane(un.b), __builtin_amdgcn_readfirstlane(un.part)};
   }
   return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
 }
@@ -823,7 +838,7 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 3 : 1) void decode_fp8_kernel(Deco
   __shared__ float sm_l[W][G];
   __shared__ float sm_acc[W > 1 ? W : 1][G][D];
 
-  const UnitId u = unit_id<W>(a);
+  const UnitId u = unit_id<W, true>(a);
   if (u.b < 0) return;
   const int g = u.g, b = u.b, part = u.part;
   const int wave = W > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -1046,7 +1061,8 @@ hipError_t launch_mfma_gb(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     int64_t per_seq = grid.z;
     if (a.window > 0 && (a.window - 1) / a.partition_size + 2 < per_seq)
       per_seq = (a.window - 1) / a.partition_size + 2;
-    const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
+    int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * per_seq;
+    if constexpr (KV8) nwg = (nwg + 8 * grid.x - 1) / (8 * grid.x) * (8 * grid.x);   // XCD-major ids
     f.flat_units = a.num_seqs <= 64 * 16 && nwg * 64 <= 0xffffffffLL;
     // column packing needs a partition's block ids in one load per lane, and
     // leaves out the window and the append (whose rows differ per sequence)
