@@ -467,6 +467,19 @@ int paged_kv_stream_read(uint32_t* checksums, const void* k_cache, const void* v
                                          static_cast<hipStream_t>(stream)), fn);
 }
 
+int pa_stream_read_contiguous(uint32_t* checksums, const void* src, uint64_t bytes, int waves, int depth,
+                              void* stream) {
+  const char* fn = "pa_stream_read_contiguous";
+  if (bytes % 16 != 0) return fail(PA_ERR_INVALID_ARG, "%s: bytes must be a multiple of 16", fn);
+  if (waves <= 0) return fail(PA_ERR_INVALID_ARG, "%s: waves must be > 0", fn);
+  if (!(depth == 1 || depth == 2 || depth == 4 || depth == 8))
+    return fail(PA_ERR_UNSUPPORTED, "%s: depth %d (1, 2, 4 or 8)", fn, depth);
+  if (bytes == 0) return ok();
+  if (!checksums || !src) return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return launch_status(pa::launch_contiguous_read(src, bytes, waves, depth, checksums,
+                                                  static_cast<hipStream_t>(stream)), fn);
+}
+
 int paged_attention_reduce_window(void* out, float* lse, const float* part_out, const float* part_lse,
                                   const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
                                   int partition_size, int max_partitions, int window, pa_dtype dtype,

@@ -145,6 +145,8 @@ hipError_t launch_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, 
 // folded into XOR checksums [B, H_kv, P]; LDS-DMA ring of `depth` slots, or
 // `depth` tiles of register loads at a time.
 hipError_t launch_stream(const DecodeArgs& a, uint32_t* sums, int depth, bool dma, hipStream_t stream);
+hipError_t launch_contiguous_read(const void* src, uint64_t bytes, int waves, int depth, uint32_t* sums,
+                                  hipStream_t stream);
 // Paged prefill: the same kernels with keys read through the block table.
 hipError_t launch_paged_prefill(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);
 hipError_t launch_paged_prefill_generic(const PrefillArgs& a, DType dt, int head_dim, hipStream_t stream);

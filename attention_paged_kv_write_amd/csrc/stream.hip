@@ -12,6 +12,10 @@
 //         flight while one is read back;
 //   VGPR: plain non-temporal 16-byte loads into registers, DEPTH tiles issued
 //         together before any is folded.
+//
+// pa_stream_read_contiguous: the plain ceiling beside it, a buffer read front
+// to back (no table, no tiles), so that the paged pattern can be told from
+// what HBM gives any read.
 #include "kernels.h"
 #include "units.h"
 
@@ -151,6 +155,31 @@ __global__ __launch_bounds__(64) void paged_stream_kernel(DecodeArgs a, uint32_t
   if (lane == 0) sums[(static_cast<size_t>(b) * a.num_kv_heads + g) * a.num_partitions + part] = acc;
 }
 
+// Wave w (one per workgroup) reads 16-byte chunks [w * cpw, min((w + 1) * cpw,
+// n)), lane l the chunks w * cpw + l + 64k, DEPTH non-temporal loads in flight
+// per lane, and writes the XOR of their 32-bit words to sums[w].
+template <int DEPTH>
+__global__ __launch_bounds__(64) void contiguous_read_kernel(const u32x4* __restrict__ src, uint64_t n, uint64_t cpw,
+                                                             uint32_t* sums) {
+  const uint64_t w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint64_t lo = w * cpw;
+  const uint64_t hi = lo + cpw < n ? lo + cpw : n;
+  uint32_t acc = 0;
+  for (uint64_t base = lo + lane; base < hi; base += 64 * DEPTH) {
+    u32x4 v[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const uint64_t idx = base + 64 * d;
+      v[d] = idx < hi ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) acc ^= xor4(v[d]);
+  }
+  for (int m = 32; m >= 1; m >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), m));
+  if (lane == 0) sums[w] = acc;
+}
+
 namespace {
 
 template <int BS, int DEPTH, bool DMA>
@@ -184,6 +213,21 @@ hipError_t launch_stream_b(const DecodeArgs& a, uint32_t* sums, int depth, bool 
 }
 
 }  // namespace
+
+hipError_t launch_contiguous_read(const void* src, uint64_t bytes, int waves, int depth, uint32_t* sums,
+                                  hipStream_t s) {
+  const uint64_t n = bytes / 16;
+  const uint64_t cpw = (n + waves - 1) / waves;
+  const u32x4* p = static_cast<const u32x4*>(src);
+  switch (depth) {
+    case 1: hipLaunchKernelGGL((contiguous_read_kernel<1>), dim3(waves), dim3(64), 0, s, p, n, cpw, sums); break;
+    case 2: hipLaunchKernelGGL((contiguous_read_kernel<2>), dim3(waves), dim3(64), 0, s, p, n, cpw, sums); break;
+    case 4: hipLaunchKernelGGL((contiguous_read_kernel<4>), dim3(waves), dim3(64), 0, s, p, n, cpw, sums); break;
+    case 8: hipLaunchKernelGGL((contiguous_read_kernel<8>), dim3(waves), dim3(64), 0, s, p, n, cpw, sums); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_stream(const DecodeArgs& a, uint32_t* sums, int depth, bool dma, hipStream_t s) {
   switch (a.block_size) {

@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "paged_prefill_window", "paged_attention_reduce_window", "paged_kv_write_fp8",
     "paged_attention_decode_fp8", "rope_cos_sin_cache", "paged_kv_write_rope",
     "paged_attention_decode_append", "paged_attention_decode_append_fp8", "paged_kv_stream_read",
-    "paged_attention_decode_noalloc",
+    "paged_attention_decode_noalloc", "pa_stream_read_contiguous",
 )
 PA_STREAM_LDS_DMA, PA_STREAM_REGISTERS = 0, 1
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # E4M3 codes, one byte each
@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_decode_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                       i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                       f32, vp, vp, i32, i32, vp]
+    lib.pa_stream_read_contiguous.restype = i32
+    lib.pa_stream_read_contiguous.argtypes = [vp, vp, ctypes.c_uint64, i32, i32, vp]
     lib.rope_cos_sin_cache.restype = i32
     lib.rope_cos_sin_cache.argtypes = [vp, i32, i32, ctypes.c_double, vp]
     lib.paged_kv_write_rope.restype = i32
@@ -450,6 +452,24 @@ def paged_kv_stream_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_tab
                                     int(depth), _dtype_code(k_cache), _stream(k_cache)))
     return checksums
 
+
+def stream_read_contiguous(src: torch.Tensor, waves: int = 2048, depth: int = 4,
+                           checksums: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The plain read ceiling: every byte of the (contiguous) device tensor src
+    read front to back in 16-byte non-temporal loads, wave w taking an equal
+    contiguous share; returns the per-wave XOR checksums (uint32 viewed as
+    int32 [waves])."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 16:
+        raise ValueError("stream_read_contiguous: the tensor's size must be a multiple of 16 bytes")
+    if checksums is None:
+        checksums = torch.empty((waves,), dtype=torch.int32, device=src.device)
+    if checksums.shape != (waves,):
+        raise ValueError("stream_read_contiguous: checksums must be [waves]")
+    _check(lib.pa_stream_read_contiguous(_dev(checksums, "checksums", torch.int32, 1), _dev(src, "src"),
+                                         nbytes, int(waves), int(depth), _stream(src)))
+    return checksums
 
 def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                    block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,

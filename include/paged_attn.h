@@ -450,6 +450,24 @@ int paged_kv_stream_read(uint32_t* checksums, const void* k_cache, const void* v
                          int num_blocks, int partition_size, int max_context_len, int mode, int depth,
                          pa_dtype dtype, void* stream);
 
+/*
+ * pa_stream_read_contiguous - a measurement call, not a step of the method: the
+ * plain read ceiling that paged_kv_stream_read's pattern is compared with.
+ *
+ * Reads bytes bytes of src front to back in 16-byte non-temporal loads, with no
+ * table and no tiles.  With n = bytes / 16 and cpw = ceil(n / waves), wave w
+ * (one per workgroup) reads the 16-byte chunks [w * cpw, min((w + 1) * cpw, n)),
+ * `depth` loads in flight per lane (1, 2, 4 or 8; else PA_ERR_UNSUPPORTED), and
+ * writes checksums[w] = XOR of every 32-bit word of its chunks (0 for a wave with
+ * none), so every fetched byte is used and the result can be checked.
+ *   src        device buffer, 16-byte aligned
+ *   checksums  uint32 [waves], device
+ * bytes must be a multiple of 16 and waves > 0 (else PA_ERR_INVALID_ARG);
+ * bytes = 0 launches nothing and leaves checksums untouched.
+ */
+int pa_stream_read_contiguous(uint32_t* checksums, const void* src, uint64_t bytes, int waves,
+                              int depth, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

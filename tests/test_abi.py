@@ -203,6 +203,16 @@ def test_append_validation(lib):
     assert lib.paged_attention_decode_append_fp8(*base(), None, p, 0, 1, None) == 1  # null scale
 
 
+def test_contiguous_read_validation(lib):
+    p = ctypes.c_void_p(16)
+    f = lib.pa_stream_read_contiguous
+    assert f(p, p, 24, 8, 4, None) == 1       # not a multiple of 16 bytes
+    assert f(p, p, 64, 0, 4, None) == 1       # no waves
+    assert f(p, p, 64, 8, 3, None) == 2       # unsupported depth
+    assert f(None, p, 64, 8, 4, None) == 1    # null checksums
+    assert f(None, None, 0, 8, 4, None) == 0  # nothing to read
+
+
 def test_stream_probe_validation(lib):
     p = ctypes.c_void_p(16)
     f = lib.paged_kv_stream_read

@@ -63,3 +63,28 @@ def test_stream_rejects_unsupported():
         ops.paged_kv_stream_read(kc, vc, bt, cl, case.max_context_len, 64, ops.PA_STREAM_LDS_DMA, 5)
     with pytest.raises(ops.PagedAttnError):
         ops.paged_kv_stream_read(kc, vc, bt, cl, case.max_context_len, 24, ops.PA_STREAM_LDS_DMA, 2)
+
+
+def host_contiguous_sums(words, waves):
+    # wave w takes the 16-byte chunks [w*cpw, min((w+1)*cpw, n)), cpw = ceil(n / waves)
+    n = words.size // 4
+    cpw = -(-n // waves)
+    out = np.zeros(waves, dtype=np.uint32)
+    for w in range(waves):
+        lo, hi = w * cpw, min((w + 1) * cpw, n)
+        if lo < hi:
+            out[w] = np.bitwise_xor.reduce(words[4 * lo:4 * hi])
+    return out
+
+
+@pytest.mark.parametrize("nbytes,waves", [(16, 1), (16 * 1000, 7), (16 * 64 * 9 + 16 * 5, 3),
+                                          ((1 << 20) + 16 * 3, 64), (16 * 10, 32)])
+def test_contiguous_read_checksums(nbytes, waves):
+    rng = np.random.default_rng(nbytes + waves)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    want = host_contiguous_sums(words, waves)
+    for depth in (1, 2, 4, 8):
+        got = ops.stream_read_contiguous(src, waves=waves, depth=depth)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want, err_msg=f"depth {depth}")
