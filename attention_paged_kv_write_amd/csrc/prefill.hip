@@ -108,30 +108,42 @@ __device__ __forceinline__ float quarter_reduce(float x, Op op) {
 // blocks; each wave owns 32 query rows (two 16-row groups) of one head, so a
 // K/V fragment read from LDS feeds two MFMAs.
 template <int NW, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int ntiles) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int group, int ntiles, int ksub) {
   constexpr int NR = 4 / NW;
   constexpr int PM = 32 * NR;   // query rows per workgroup
   constexpr int RG = 2;         // 16-row groups per wave
   // two K/V tiles: per tile K rows (64 x 16 chunks of 16 B) then V rows
   __shared__ __attribute__((aligned(16))) u32x4 kvbuf[2 * 2048];
 
-  // Workgroup -> (head column, sequence, q tile).  Workgroups are dealt to the
-  // 8 XCDs round-robin, so the XCD is the id mod 8: head column c (KV head g,
-  // head block hb) lives on XCD c mod 8, and its workgroups run sequence by
-  // sequence, q tiles longest-first within a sequence.  Concurrent workgroups
-  // of an XCD thus stream the same K/V prefix through its L2.
+  // Workgroup -> (head column, sequence, q tile).  Workgroups are dealt to
+  // the 8 XCDs round-robin (the XCD is the id mod 8), and the column is the
+  // id mod ncol, so with ncol a multiple of 8 head column c (KV head g, head
+  // block hb) lives on XCD c mod 8.  With ncol a divisor of 8, 8 / ncol XCDs
+  // share a column: with enough sequences (ksub = 8 / ncol) XCD col + k *
+  // ncol takes the sequences s = k mod ksub whole; otherwise (ksub = 1) a
+  // column's consecutive items alternate over its XCDs, each taking every
+  // (8 / ncol)-th q tile of every sequence, so that one long sequence still
+  // spreads over all XCDs.  Either way an XCD's workgroups run sequence by
+  // sequence, q tiles longest-first within a sequence, its concurrent
+  // workgroups stream the same K/V prefix through its L2, and every XCD has
+  // work.
   const int Hkv = a.num_kv_heads;
   const int nhb = group / NW;   // head blocks per KV group
   const int ncol = Hkv * nhb;
-  const int cpx = (ncol + 7) >> 3;   // head columns per XCD
   const int id = blockIdx.x;
-  const int xcd = id & 7;
-  int r = id >> 3;
-  const int col = (r % cpx) * 8 + xcd;
-  r /= cpx;
-  if (col >= ncol) return;
+  const int col = id % ncol;
   const int g = col % Hkv, hb = col / Hkv;
-  const int s = r / ntiles, w = r % ntiles;
+  int s, w;
+  if (ksub > 1) {
+    const int t = id / ncol;
+    const int u = t / ksub;
+    w = u % ntiles;
+    s = (u / ntiles) * ksub + t % ksub;
+  } else {
+    const int r = id / ncol;
+    s = r / ntiles;
+    w = r % ntiles;
+  }
   if (s >= a.num_seqs) return;
   const SeqSpan sp = seq_span(a, s);
   const int qt = (sp.len + PM - 1) / PM - 1 - w;
@@ -604,13 +616,19 @@ hipError_t launch_mfma(const PrefillArgs& a, int group, hipStream_t s) {
   const int pm = 32 * (4 / nw);            // query rows per workgroup
   const int ntiles = (a.max_seqlen + pm - 1) / pm;
   const int ncol = a.num_kv_heads * (group / nw);
-  const int64_t n = 8LL * ((ncol + 7) / 8) * a.num_seqs * ntiles;
+  // XCDs sharing a column take whole sequences when each gets four or more
+  // (64 sequences of 512 tokens over 2 columns: 499 against 411 TFLOP/s with
+  // q tiles interleaved); one long sequence keeps the interleave (8,192
+  // tokens: 670 against 261).
+  const int share = (ncol < 8 && 8 % ncol == 0) ? 8 / ncol : 1;
+  const int ksub = a.num_seqs >= 4 * share ? share : 1;
+  const int64_t n = static_cast<int64_t>(ncol) * ksub * ((a.num_seqs + ksub - 1) / ksub) * ntiles;
   if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
   const dim3 grid(static_cast<unsigned>(n));
   switch (nw) {
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
-    default: hipLaunchKernelGGL((prefill_mfma_kernel<1, PAGED>), grid, dim3(256), 0, s, a, group, ntiles); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<4, PAGED>), grid, dim3(256), 0, s, a, group, ntiles, ksub); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<2, PAGED>), grid, dim3(256), 0, s, a, group, ntiles, ksub); break;
+    default: hipLaunchKernelGGL((prefill_mfma_kernel<1, PAGED>), grid, dim3(256), 0, s, a, group, ntiles, ksub); break;
   }
   return hipGetLastError();
 }

@@ -39,6 +39,12 @@ PREFILL_CASES = {
                     num_kv_heads=2, head_dim=64),
     "bf16_d64": dict(num_seqs=3, lens_fixed=(3, 40, 90), num_q_heads=4, num_kv_heads=2, head_dim=64),
     "f32_d128": dict(dtype=wl.F32, num_seqs=2, lens_fixed=(31, 77), num_q_heads=8, num_kv_heads=2),
+    # fewer head columns than XCDs: 2 columns shared by 4 XCDs each, whole
+    # sequences dealt to them (18 sequences) or q tiles interleaved (3)
+    "two_columns_dealt": dict(num_seqs=18, len_min=1, len_max=300, num_q_heads=8, num_kv_heads=1),
+    "two_columns_interleaved": dict(num_seqs=3, lens_fixed=(700, 1, 333), num_q_heads=8, num_kv_heads=2),
+    # one column over all 8 XCDs, 33 sequences dealt
+    "one_column_dealt": dict(num_seqs=33, len_min=0, len_max=200, num_q_heads=4, num_kv_heads=1),
 }
 
 
