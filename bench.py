@@ -650,6 +650,38 @@ def main(argv=None):
                                        "by_length": sweep}
             log("prefill length sweep (TFLOP/s): " + ", ".join(f"{k}: {v['tflops']}" for k, v in sweep.items()))
 
+            # The workload's own lengths at Llama-3-8B's heads per GPU under 4- and
+            # 8-way tensor parallelism (H_q 8 with H_kv 2 or 1): fewer head columns
+            # than XCDs, so the XCDs share each column.
+            cu_d = torch.from_numpy(pc.cu_seqlens).to(dev)
+            lens_h = np.diff(pc.cu_seqlens).astype(np.int64)
+            few = {}
+            for hq, hkv in ((8, 2), (8, 1)):
+                fq, fk, fv = draw((T_, hq, d_)), draw((T_, hkv, d_)), draw((T_, hkv, d_))
+                fo = torch.empty_like(fq)
+                fl = torch.empty((T_, hq), dtype=torch.float32, device=dev)
+
+                def ffill():
+                    ops.varlen_causal_prefill(fq, fk, fv, cu_d, pc.max_seqlen, pc.scale, out=fo, lse=fl)
+                for _ in range(2):
+                    ffill()
+                torch.cuda.synchronize()
+                sa, sb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                sa.record(stream)
+                for _ in range(10):
+                    ffill()
+                sb.record(stream)
+                torch.cuda.synchronize()
+                fms = sa.elapsed_time(sb) / 10
+                ftf = 4.0 * d_ * hq * float((lens_h * (lens_h + 1) // 2).sum()) / (fms * 1e-3) / 1e12
+                few[f"hq{hq}_hkv{hkv}"] = {"kernel_avg_us": round(fms * 1e3, 1), "tflops": round(ftf, 1),
+                                           "frac": round(ftf / BF16_PEAK_TFLOPS, 4)}
+                del fq, fk, fv, fo, fl
+            torch.cuda.empty_cache()
+            prefill["few_kv_heads"] = {"lengths": pc.spec.name + " (same cu_seqlens)",
+                                       "values": "iid standard normal, bf16, drawn on the device", "by_heads": few}
+            log("prefill, few KV heads (TFLOP/s): " + ", ".join(f"{k}: {v['tflops']}" for k, v in few.items()))
+
             # The rate the matrix cores sustain on this machine for a plain bf16 GEMM
             # (torch.matmul, 8192^3): the clock under dense matrix work sits well
             # below the 2.4 GHz the 2.5 PFLOP/s peak assumes, so this is the
