@@ -119,11 +119,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // the 8 XCDs round-robin (the XCD is the id mod 8), and the column is the
   // id mod ncol, so with ncol a multiple of 8 head column c (KV head g, head
   // block hb) lives on XCD c mod 8.  With ncol a divisor of 8, 8 / ncol XCDs
-  // share a column: with enough sequences (ksub = 8 / ncol) XCD col + k *
-  // ncol takes the sequences s = k mod ksub whole; otherwise (ksub = 1) a
-  // column's consecutive items alternate over its XCDs, each taking every
-  // (8 / ncol)-th q tile of every sequence, so that one long sequence still
-  // spreads over all XCDs.  Either way an XCD's workgroups run sequence by
+  // share a column: when the launcher expects that to stay even (ksub = 8 /
+  // ncol) XCD col + k * ncol takes the sequences s = k mod ksub whole;
+  // otherwise (ksub = 1) a column's consecutive items alternate over its
+  // XCDs, each taking every (8 / ncol)-th q tile of every sequence, so that
+  // one long sequence or a few uneven ones still spread evenly.  Either way
+  // an XCD's workgroups run sequence by
   // sequence, q tiles longest-first within a sequence, its concurrent
   // workgroups stream the same K/V prefix through its L2, and every XCD has
   // work.
@@ -616,12 +617,19 @@ hipError_t launch_mfma(const PrefillArgs& a, int group, hipStream_t s) {
   const int pm = 32 * (4 / nw);            // query rows per workgroup
   const int ntiles = (a.max_seqlen + pm - 1) / pm;
   const int ncol = a.num_kv_heads * (group / nw);
-  // XCDs sharing a column take whole sequences when each gets four or more
-  // (64 sequences of 512 tokens over 2 columns: 499 against 411 TFLOP/s with
-  // q tiles interleaved); one long sequence keeps the interleave (8,192
-  // tokens: 670 against 261).
+  // XCDs sharing a column (ncol a divisor of 8) take whole sequences when
+  // that should keep them even: at least one sequence each, and either
+  // lengths close to equal (mean at least 0.8 of the maximum) or sixteen
+  // sequences or more each.  Dealt against interleaved, 2 columns, same box:
+  // 64 x 512 tokens 498-500 against 408 TFLOP/s, 16 x 2,048 757-798 against
+  // 651-674, 128 sequences of 64-1,024 tokens 508-510 against 402-422; the
+  // 16 uneven sequences of the Llama-3-8B varlen mix (mean 0.6 of the
+  // maximum), where dealing leaves one XCD pair 1.38x the mean work, 479-486
+  // against 523-530; one 8,192-token sequence 261 against 670.
   const int share = (ncol < 8 && 8 % ncol == 0) ? 8 / ncol : 1;
-  const int ksub = a.num_seqs >= 4 * share ? share : 1;
+  const int64_t S = a.num_seqs;
+  const bool even = 5LL * a.total_tokens >= 4LL * S * a.max_seqlen || S >= 16LL * share;
+  const int ksub = (share > 1 && S >= share && even) ? share : 1;
   const int64_t n = static_cast<int64_t>(ncol) * ksub * ((a.num_seqs + ksub - 1) / ksub) * ntiles;
   if (n * 256 > 0xffffffffLL) return hipErrorInvalidValue;   // total threads of a launch
   const dim3 grid(static_cast<unsigned>(n));
