@@ -22,9 +22,10 @@
 // lanes) instead of 32-64-byte pieces of 16 rows.
 //
 // Scheduling: workgroups are dealt to the 8 XCDs round-robin; the kernel maps
-// its id so that one head column (KV head, head block) stays on one XCD and
-// that XCD runs the q tiles of one sequence (longest first) back to back, so
-// the concurrent workgroups of an XCD stream the same K/V prefix through its L2.
+// its id so that one head column (KV head, head block) stays on one XCD (or,
+// with fewer than 8 columns, on the XCDs that share it) and that XCD runs the
+// q tiles of one sequence (longest first) back to back, so the concurrent
+// workgroups of an XCD stream the same K/V prefix through its L2.
 //
 // prefill_generic_kernel (fp32 or bf16, head_dim 64/128): vector ALU, one wave
 // per query row, LPT lanes per key row, online softmax per row group.
