@@ -103,29 +103,42 @@ __global__ __launch_bounds__(256) void reduce_small_kernel(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;  // b * H_q + h
   if (row >= static_cast<size_t>(a.num_seqs) * a.num_q_heads) return;
-  const int b = static_cast<int>(row / a.num_q_heads);
-  const int64_t ctx = max(a.context_lens[b], 0);
-  const int64_t first = a.window > 0 ? max<int64_t>(0, ctx - a.window) / a.partition_size : 0;
-  const int64_t live = min<int64_t>((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
-  const int n = static_cast<int>(min<int64_t>(max<int64_t>(0, live - first), MAXP));
-  const float* lse_row = a.part_lse + row * a.max_partitions + first;
-  const float* out_row = a.part_out + (row * a.max_partitions + first) * D + lane * DPL;
-  const float my_lse = lane < n ? lse_row[lane] : kNegInf;
+  // (rows fit 32 bits: the grid holds at most 2^32 / 64 waves)
+  const int b = static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(a.num_q_heads));
+  float got_lse = kNegInf;
   float o[MAXP][DPL];
+  // Load partitions first .. first + nl - 1 of this row.
+  auto load = [&](int64_t first, int nl) {
+    const float* lse_row = a.part_lse + row * a.max_partitions + first;
+    const float* out_row = a.part_out + (row * a.max_partitions + first) * D + lane * DPL;
+    got_lse = lane < nl ? lse_row[lane] : kNegInf;
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
+    for (int p = 0; p < MAXP; ++p) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[p][e] = 0.f;
-    if (p < n) {
-      if constexpr (DPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(out_row + static_cast<size_t>(p) * D);
-        o[p][0] = v.x;
-        o[p][1] = v.y;
-      } else {
-        o[p][0] = out_row[static_cast<size_t>(p) * D];
+      for (int e = 0; e < DPL; ++e) o[p][e] = 0.f;
+      if (p < nl) {
+        if constexpr (DPL == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(out_row + static_cast<size_t>(p) * D);
+          o[p][0] = v.x;
+          o[p][1] = v.y;
+        } else {
+          o[p][0] = out_row[static_cast<size_t>(p) * D];
+        }
       }
     }
-  }
+  };
+  // Without a window the merge starts at partition 0, so its loads need not
+  // wait for the context length: every allocated partition (up to MAXP) is
+  // read at once and the ones past the sequence's end are masked below.  A
+  // window's first partition depends on the context length.
+  const bool nowin = a.window <= 0;
+  if (nowin) load(0, static_cast<int>(min<int64_t>(a.max_partitions, MAXP)));
+  const int64_t ctx = max(a.context_lens[b], 0);
+  const int64_t first = nowin ? 0 : max<int64_t>(0, ctx - a.window) / a.partition_size;
+  const int64_t live = min<int64_t>((ctx + a.partition_size - 1) / a.partition_size, a.max_partitions);
+  const int n = static_cast<int>(min<int64_t>(max<int64_t>(0, live - first), MAXP));
+  if (!nowin) load(first, n);
+  const float my_lse = lane < n ? got_lse : kNegInf;
   const float M = group_allreduce<64>(my_lse, OpMax());
   float acc[DPL], wsum = 0.f;
 #pragma unroll
