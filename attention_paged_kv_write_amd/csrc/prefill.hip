@@ -125,10 +125,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a, int
   // otherwise (ksub = 1) a column's consecutive items alternate over its
   // XCDs, each taking every (8 / ncol)-th q tile of every sequence, so that
   // one long sequence or a few uneven ones still spread evenly.  Either way
-  // an XCD's workgroups run sequence by
-  // sequence, q tiles longest-first within a sequence, its concurrent
-  // workgroups stream the same K/V prefix through its L2, and every XCD has
-  // work.
+  // an XCD's workgroups run sequence by sequence, q tiles longest-first
+  // within a sequence, its concurrent workgroups stream the same K/V prefix
+  // through its L2, and every XCD has work.
   const int Hkv = a.num_kv_heads;
   const int nhb = group / NW;   // head blocks per KV group
   const int ncol = Hkv * nhb;

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void reduce_small_kernel(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const size_t row = static_cast<size_t>(blockIdx.x) * 4 + wave;  // b * H_q + h
   if (row >= static_cast<size_t>(a.num_seqs) * a.num_q_heads) return;
-  // (rows fit 32 bits: the grid holds at most 2^32 / 64 waves)
+  // (rows fit 32 bits: the call rejects more than INT32_MAX of them)
   const int b = static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(a.num_q_heads));
   float got_lse = kNegInf;
   float o[MAXP][DPL];
