@@ -28,6 +28,9 @@ OFFSET = (1 << 35) + (16 << 20)       # live blocks start past 32 GiB
 
 @pytest.fixture(scope="module")
 def big_pools():
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * POOL_BYTES + (4 << 30):
+        pytest.skip(f"needs {2 * POOL_BYTES / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
     print(f"allocating two pools of {POOL_BYTES / 2**30:.2f} GiB", flush=True)
     k = torch.empty(POOL_BYTES, dtype=torch.uint8, device="cuda")
     v = torch.empty(POOL_BYTES, dtype=torch.uint8, device="cuda")
