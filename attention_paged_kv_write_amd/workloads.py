@@ -496,7 +496,7 @@ LLAMA3_8B_DECODE_FP8 = replace(
     LLAMA3_8B_DECODE, name="llama3_8b_paged_decode_fp8_e4m3", kv_dtype=E4M3,
     k_scale=6.0 / 448.0, v_scale=5.0 / 448.0)
 
-CONFIGS = {
+WORKLOADS = {
     1: TINY_DECODE_F32,
     2: LLAMA3_8B_DECODE,
     3: LLAMA3_8B_PREFILL,
@@ -508,16 +508,16 @@ CONFIGS = {
 }
 
 
-def seed_for(config_index: int) -> int:
-    return 1000 + config_index
+def seed_for(index: int) -> int:
+    return 1000 + index
 
 
-def make_case(config_index: int, seed: Optional[int] = None, **overrides):
-    """Build workload ``config_index`` (1..8), optionally shrunk by overrides."""
-    spec = CONFIGS[config_index]
+def make_case(index: int, seed: Optional[int] = None, **overrides):
+    """Build workload ``index`` (1..8), optionally shrunk by overrides."""
+    spec = WORKLOADS[index]
     if overrides:
         spec = replace(spec, **overrides)
-    s = seed_for(config_index) if seed is None else seed
+    s = seed_for(index) if seed is None else seed
     if isinstance(spec, PrefillSpec):
         return make_prefill_case(spec, s)
     if isinstance(spec, PagedPrefillSpec):
