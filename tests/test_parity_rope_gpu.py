@@ -58,10 +58,10 @@ def run_fused(case, dtype, rot, P=4096):
     return (dq, dk, kc, vc), ref, pos
 
 
-def fp32_term(x, pos, rot, dtype):
+def fp32_term(x, pos, rot, dtype, base=BASE):
     """4 fp32 ulps of |x1 c| + |x2 s| per rotated element (0 past rot_dim)."""
     xa = np.abs(oracle.upcast(x, dtype))
-    tab = np.abs(rope.cos_sin_table(int(np.max(pos)) + 1, rot, BASE))[np.asarray(pos)][:, None, :]
+    tab = np.abs(rope.cos_sin_table(int(np.max(pos)) + 1, rot, base))[np.asarray(pos)][:, None, :]
     h = rot // 2
     m1 = xa[..., :h] * tab[..., :h] + xa[..., h:rot] * tab[..., h:]
     m2 = xa[..., h:rot] * tab[..., :h] + xa[..., :h] * tab[..., h:]
@@ -70,9 +70,9 @@ def fp32_term(x, pos, rot, dtype):
     return 4 * 2.0 ** -24 * out
 
 
-def check_rotated(gpu_t, ref_bits, x, pos, rot, dtype, what):
-    ref64 = rope.rotate(x, pos, rot, BASE, dtype)
-    bound = fp32_term(x, pos, rot, dtype)
+def check_rotated(gpu_t, ref_bits, x, pos, rot, dtype, what, base=BASE):
+    ref64 = rope.rotate(x, pos, rot, base, dtype)
+    bound = fp32_term(x, pos, rot, dtype, base)
     if dtype == wl.BF16:
         g = to_host_bits(gpu_t)
         err = np.abs(wl.bf16_bits_to_f32(g).astype(np.float64) - ref64)
