@@ -30,11 +30,14 @@ CASES = {
                     num_q_heads=4, num_kv_heads=2, head_dim=64),
     "bf16_d64": dict(num_seqs=2, prefix_fixed=(12, 70), chunk_fixed=(20, 45), num_q_heads=4,
                      num_kv_heads=2, head_dim=64),
-    # fewer head columns than XCDs (whole sequences dealt to the XCDs sharing one)
-    "two_columns_dealt": dict(num_seqs=17, prefix_min=0, prefix_max=300, chunk_min=1, chunk_max=150,
+    # fewer head columns than XCDs: whole sequences dealt to the XCDs sharing a
+    # column (chunks of near-equal length) or q tiles interleaved (uneven ones)
+    "two_columns_dealt": dict(num_seqs=17, prefix_min=0, prefix_max=300, chunk_min=130, chunk_max=150,
                               num_q_heads=8, num_kv_heads=1),
-    "one_column_dealt": dict(num_seqs=32, prefix_min=0, prefix_max=100, chunk_min=1, chunk_max=80,
+    "one_column_dealt": dict(num_seqs=32, prefix_min=0, prefix_max=100, chunk_min=70, chunk_max=80,
                              num_q_heads=2, num_kv_heads=1, block_size=32),
+    "two_columns_interleaved": dict(num_seqs=17, prefix_min=0, prefix_max=300, chunk_min=1, chunk_max=150,
+                                    num_q_heads=8, num_kv_heads=1),
 }
 
 

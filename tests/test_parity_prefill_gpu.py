@@ -40,11 +40,16 @@ PREFILL_CASES = {
     "bf16_d64": dict(num_seqs=3, lens_fixed=(3, 40, 90), num_q_heads=4, num_kv_heads=2, head_dim=64),
     "f32_d128": dict(dtype=wl.F32, num_seqs=2, lens_fixed=(31, 77), num_q_heads=8, num_kv_heads=2),
     # fewer head columns than XCDs: 2 columns shared by 4 XCDs each, whole
-    # sequences dealt to them (18 sequences) or q tiles interleaved (3)
-    "two_columns_dealt": dict(num_seqs=18, len_min=1, len_max=300, num_q_heads=8, num_kv_heads=1),
+    # sequences dealt to them (18 of near-equal length: the launcher deals when
+    # the mean length is at least 0.8 of the longest) or q tiles interleaved
+    # (3 uneven ones)
+    "two_columns_dealt": dict(num_seqs=18, lens_fixed=(300, 290, 281, 299, 250, 300, 257, 264, 300, 295, 288,
+                                                       270, 241, 300, 299, 262, 277, 300),
+                              num_q_heads=8, num_kv_heads=1),
     "two_columns_interleaved": dict(num_seqs=3, lens_fixed=(700, 1, 333), num_q_heads=8, num_kv_heads=2),
-    # one column over all 8 XCDs, 33 sequences dealt
-    "one_column_dealt": dict(num_seqs=33, len_min=0, len_max=200, num_q_heads=4, num_kv_heads=1),
+    # one column over all 8 XCDs, 33 sequences dealt (one of them empty)
+    "one_column_dealt": dict(num_seqs=33, lens_fixed=(0,) + tuple(190 + (7 * i) % 11 for i in range(32)),
+                             num_q_heads=4, num_kv_heads=1),
 }
 
 
