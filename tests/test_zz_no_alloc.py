@@ -50,6 +50,30 @@ def test_noalloc_matches_split_decode_twice(window):
 
 
 @pytest.mark.gpu
+def test_noalloc_f32_vector_kernels_twice():
+    # fp32 queries and pools at head_dim 64 (the vector decode kernel and the
+    # fp32 merge), GQA group 4, 32-token blocks, under a window on the second call
+    big = wl.make_case(1, batch=9, ctx_fixed=None, ctx_min=1, ctx_max=900, num_q_heads=8, num_kv_heads=2,
+                       block_size=32, num_blocks=None, max_blocks_per_seq=29)
+    small = wl.make_case(1, seed=78, batch=3, ctx_fixed=(1, 64, 300), num_q_heads=8, num_kv_heads=2,
+                         block_size=32, num_blocks=None, max_blocks_per_seq=10)
+    for case, ps, window in ((big, 128, 0), (small, 64, 100)):
+        (q, kc, vc, bt, cl), ref_out, ref_lse = _reference(case, ps, window)
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device)
+        ops.paged_attention_decode_noalloc(q, kc, vc, bt, cl, case.max_context_len, case.scale, ps, out, lse,
+                                           window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), (ps, window)
+        assert torch.equal(lse, ref_lse), (ps, window)
+        ek, ev = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping,
+                                 case.spec.block_size)
+        o_out, o_lse = oracle.decode(case.q, ek, ev, case.block_tables, case.context_lens, case.spec.block_size,
+                                     case.scale, case.spec.dtype, window=window)
+        assert_parity(to_host_f64(out), to_host_f64(lse), o_out, o_lse, case.spec.dtype, f"noalloc f32 ps={ps}")
+
+
+@pytest.mark.gpu
 def test_noalloc_in_a_hip_graph():
     # the call as its callers make it under graph capture: captured once, then
     # replayed three times with eager work (refilling the outputs with NaN)
