@@ -14,8 +14,12 @@ Pools written on the GPU are compared bit for bit with the oracle's write.
 
 The draws are host logic: a CPU test checks that they are valid and that
 together they reach every value listed above.
+A wide regime (up to 8 KV heads, 24 sequences, contexts to 8,192, prompts to
+1,500, cached prefixes to 3,000, windows to 3,000) adds a few draws of each
+kind; PA_PARITY_DRAWS=k multiplies every count for a longer sweep.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -26,7 +30,17 @@ from attention_paged_kv_write_amd import ops
 from attention_paged_kv_write_amd import workloads as wl
 from tests.gpu_util import assert_parity, to_dev, to_host_bits, to_host_f64
 
-N_DECODE, N_PREFILL, N_PAGED, N_FP8 = 200, 100, 100, 60
+# PA_PARITY_DRAWS=k multiplies every count below (a longer sweep); the wide
+# regime (contexts to 8192, batches to 24, windows to 3000) has few draws by
+# default since its oracle side takes about a second a case.
+SCALE = max(1, int(os.environ.get("PA_PARITY_DRAWS", "1")))
+N_DECODE, N_PREFILL, N_PAGED, N_FP8 = 200 * SCALE, 100 * SCALE, 100 * SCALE, 60 * SCALE
+W_DECODE, W_PREFILL, W_PAGED, W_FP8 = 16 * SCALE, 10 * SCALE, 8 * SCALE, 6 * SCALE
+
+NARROW = dict(seed=0, hkv=5, batch=9, ctx=1200, window=301, parts=(1, 2, 4, 8, 16), fp8_parts=(1, 2, 4, 8),
+              seqs=7, prompt=400, prefix=400, chunk=250)
+WIDE = dict(seed=10000, hkv=9, batch=25, ctx=8192, window=3001, parts=(1, 4, 16, 32), fp8_parts=(1, 4, 16),
+            seqs=25, prompt=1500, prefix=3000, chunk=800)
 
 
 def _lengths(rng, n, hi, allow_zero=True):
@@ -50,95 +64,99 @@ def _scale(rng, d):
     return float(np.float32(rng.uniform(0.5, 2.0) / math.sqrt(d)))
 
 
-def _window(rng):
-    return 0 if rng.random() < 0.5 else int(rng.choice([1, 2, int(rng.integers(3, 301))]))
+def _window(rng, hi=301):
+    return 0 if rng.random() < 0.5 else int(rng.choice([1, 2, int(rng.integers(3, hi))]))
 
 
-def decode_draw(i):
-    rng = np.random.default_rng(7100 + i)
+def decode_draw(i, rg=NARROW):
+    rng = np.random.default_rng(7100 + rg["seed"] + i)
     dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
     d = int(rng.choice([64, 128]))
     G = int(rng.choice([1, 2, 4, 8]))
-    Hkv = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, rg["hkv"]))
     bs = int(rng.choice([8, 16, 32, 64]))
-    B = int(rng.integers(1, 9))
-    ctx = _lengths(rng, B, 1200)
+    B = int(rng.integers(1, rg["batch"]))
+    ctx = _lengths(rng, B, rg["ctx"])
     if max(ctx) == 0:
         ctx[0] = int(rng.integers(1, 300))
     nblk = max(-(-c // bs) for c in ctx)
     mbps = nblk + int(rng.integers(0, 4))
     maxctx = int(rng.integers(max(ctx), mbps * bs + 1))
-    window = _window(rng)
+    window = _window(rng, rg["window"])
     return dict(
-        seed=9100 + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs,
+        seed=9100 + rg["seed"] + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs,
         batch=B, ctx_fixed=tuple(ctx), max_blocks_per_seq=mbps, max_context_len=maxctx,
-        partition_size=0 if rng.random() < 0.35 else bs * int(rng.choice([1, 2, 4, 8, 16])),
+        partition_size=0 if rng.random() < 0.35 else bs * int(rng.choice(rg["parts"])),
         window=window, free_before_window=bool(window and rng.random() < 0.5),
         v_dist=str(rng.choice(["normal", "uniform"])), scale=_scale(rng, d),
         append=bool(rng.random() < 0.3), vector=bool(dtype == wl.BF16 and d == 128 and rng.random() < 0.3),
         pool_factor=float(rng.choice([1.0, 1.25, 2.0])))
 
 
-def fp8_draw(i):
-    rng = np.random.default_rng(7400 + i)
+def fp8_draw(i, rg=NARROW):
+    rng = np.random.default_rng(7400 + rg["seed"] + i)
     G = int(rng.choice([1, 2, 4, 8]))
-    Hkv = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, rg["hkv"]))
     bs = int(rng.choice([16, 32, 64]))
-    B = int(rng.integers(1, 9))
-    ctx = _lengths(rng, B, 1200)
+    B = int(rng.integers(1, rg["batch"]))
+    ctx = _lengths(rng, B, rg["ctx"])
     if max(ctx) == 0:
         ctx[0] = int(rng.integers(1, 300))
     nblk = max(-(-c // bs) for c in ctx)
     mbps = nblk + int(rng.integers(0, 4))
-    window = _window(rng)
+    window = _window(rng, rg["window"])
     return dict(
-        seed=9400 + i, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs, batch=B, ctx_fixed=tuple(ctx),
+        seed=9400 + rg["seed"] + i, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs, batch=B, ctx_fixed=tuple(ctx),
         max_blocks_per_seq=mbps, max_context_len=int(rng.integers(max(ctx), mbps * bs + 1)),
-        partition_size=0 if rng.random() < 0.35 else bs * int(rng.choice([1, 2, 4, 8])),
+        partition_size=0 if rng.random() < 0.35 else bs * int(rng.choice(rg["fp8_parts"])),
         window=window, free_before_window=bool(window and rng.random() < 0.5),
         k_scale=float(rng.uniform(2.0, 8.0) / 448.0), v_scale=float(rng.uniform(2.0, 8.0) / 448.0),
         v_dist=str(rng.choice(["normal", "uniform"])), scale=_scale(rng, 128))
 
 
-def prefill_draw(i):
-    rng = np.random.default_rng(7200 + i)
+def prefill_draw(i, rg=NARROW):
+    rng = np.random.default_rng(7200 + rg["seed"] + i)
     dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
     d = int(rng.choice([64, 128]))
     G = int(rng.choice([1, 2, 4, 8]))
-    Hkv = int(rng.integers(1, 5))
-    S = int(rng.integers(1, 7))
-    lens = _lengths(rng, S, 400)
+    Hkv = int(rng.integers(1, rg["hkv"]))
+    S = int(rng.integers(1, rg["seqs"]))
+    lens = _lengths(rng, S, rg["prompt"])
     if max(lens) == 0:
         lens[0] = int(rng.integers(1, 200))
     T = sum(lens)
     return dict(
-        seed=9200 + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, num_seqs=S,
-        lens_fixed=tuple(lens), max_seqlen=int(rng.integers(max(lens), T + 1)), window=_window(rng),
+        seed=9200 + rg["seed"] + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, num_seqs=S,
+        lens_fixed=tuple(lens), max_seqlen=int(rng.integers(max(lens), T + 1)), window=_window(rng, rg["window"]),
         scale=_scale(rng, d), vector=bool(dtype == wl.BF16 and d == 128 and rng.random() < 0.3))
 
 
-def paged_draw(i):
-    rng = np.random.default_rng(7300 + i)
+def paged_draw(i, rg=NARROW):
+    rng = np.random.default_rng(7300 + rg["seed"] + i)
     dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
     d = int(rng.choice([64, 128]))
     G = int(rng.choice([1, 2, 4, 8]))
-    Hkv = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, rg["hkv"]))
     bs = int(rng.choice([8, 16, 32, 64]))
-    S = int(rng.integers(1, 7))
-    prefix = _lengths(rng, S, 400)
-    chunk = _lengths(rng, S, 250)
+    S = int(rng.integers(1, rg["seqs"]))
+    prefix = _lengths(rng, S, rg["prefix"])
+    chunk = _lengths(rng, S, rg["chunk"])
     if max(chunk) == 0:
         chunk[0] = int(rng.integers(1, 100))
     T = sum(chunk)
     ctx = [p + c for p, c in zip(prefix, chunk)]
     mbps = max(1, max(-(-c // bs) for c in ctx))
     return dict(
-        seed=9300 + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs,
+        seed=9300 + rg["seed"] + i, dtype=dtype, head_dim=d, num_q_heads=G * Hkv, num_kv_heads=Hkv, block_size=bs,
         num_seqs=S, prefix_fixed=tuple(prefix), chunk_fixed=tuple(chunk),
         max_seqlen_q=int(rng.integers(max(chunk), T + 1)),
-        max_context_len=int(rng.integers(max(ctx), mbps * bs + 1)), window=_window(rng),
+        max_context_len=int(rng.integers(max(ctx), mbps * bs + 1)), window=_window(rng, rg["window"]),
         scale=_scale(rng, d), vector=bool(dtype == wl.BF16 and d == 128 and rng.random() < 0.3))
 
+
+def _cases(tag, n_narrow, n_wide):
+    return ([pytest.param(NARROW, i, id=f"{tag}{i:02d}") for i in range(n_narrow)] +
+            [pytest.param(WIDE, i, id=f"wide_{tag}{i:02d}") for i in range(n_wide)])
 
 _HOST_KEYS = ("seed", "max_context_len", "max_seqlen", "max_seqlen_q", "scale", "append", "vector")
 
@@ -191,15 +209,24 @@ def test_random_draws_are_valid_and_cover_the_space():
     assert any(c["append"] and c["partition_size"] and c["window"] for c in dec)
     assert any(c["max_seqlen"] > max(c["lens_fixed"]) for c in pre)
     assert any(c["max_seqlen_q"] > max(c["chunk_fixed"]) for c in pag)
+    # the wide regime reaches what the narrow one does not
+    wd = [decode_draw(i, WIDE) for i in range(W_DECODE)] + [fp8_draw(i, WIDE) for i in range(W_FP8)]
+    wp = [prefill_draw(i, WIDE) for i in range(W_PREFILL)]
+    wg = [paged_draw(i, WIDE) for i in range(W_PAGED)]
+    for c in wd:
+        assert max(c["ctx_fixed"]) <= c["max_context_len"] <= c["max_blocks_per_seq"] * c["block_size"]
+    assert max(max(c["ctx_fixed"]) for c in wd) > 4096 and max(c["window"] for c in wd) > 1000
+    assert max(c["num_kv_heads"] for c in wd + wp + wg) > 4 and max(c["batch"] for c in wd) > 8
+    assert max(max(c["lens_fixed"]) for c in wp) > 400 and max(max(c["prefix_fixed"]) for c in wg) > 400
 
 
 # ---------------------------------------------------------------------------
 # decode (+ reduce), bf16 / f32 pools
 # ---------------------------------------------------------------------------
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_DECODE), ids=lambda i: f"decode{i:02d}")
-def test_random_decode(i):
-    draw = decode_draw(i)
+@pytest.mark.parametrize("rg,i", _cases("decode", N_DECODE, W_DECODE))
+def test_random_decode(rg, i):
+    draw = decode_draw(i, rg)
     print("decode", draw, flush=True)
     case = wl.make_case(2, seed=draw["seed"], name="random_decode", **_spec_args(draw))
     sp, bs, ps, window = case.spec, case.spec.block_size, draw["partition_size"], draw["window"]
@@ -241,9 +268,9 @@ def test_random_decode(i):
 # decode over E4M3 pools (bf16 queries, head_dim 128)
 # ---------------------------------------------------------------------------
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_FP8), ids=lambda i: f"fp8_{i:02d}")
-def test_random_decode_fp8(i):
-    draw = fp8_draw(i)
+@pytest.mark.parametrize("rg,i", _cases("fp8_", N_FP8, W_FP8))
+def test_random_decode_fp8(rg, i):
+    draw = fp8_draw(i, rg)
     print("fp8 decode", draw, flush=True)
     case = wl.make_case(8, seed=draw["seed"], name="random_fp8", **_spec_args(draw))
     bs, ps, window, maxctx, scale = (case.spec.block_size, draw["partition_size"], draw["window"],
@@ -283,9 +310,9 @@ def test_random_decode_fp8(i):
 # varlen causal prefill
 # ---------------------------------------------------------------------------
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_PREFILL), ids=lambda i: f"prefill{i:02d}")
-def test_random_prefill(i):
-    draw = prefill_draw(i)
+@pytest.mark.parametrize("rg,i", _cases("prefill", N_PREFILL, W_PREFILL))
+def test_random_prefill(rg, i):
+    draw = prefill_draw(i, rg)
     print("prefill", draw, flush=True)
     window, scale = draw["window"], draw["scale"]
     case = wl.make_case(3, seed=draw["seed"], name="random_prefill",
@@ -308,9 +335,9 @@ def test_random_prefill(i):
 # paged (chunked / prefix-cached) prefill
 # ---------------------------------------------------------------------------
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(N_PAGED), ids=lambda i: f"paged{i:02d}")
-def test_random_paged_prefill(i):
-    draw = paged_draw(i)
+@pytest.mark.parametrize("rg,i", _cases("paged", N_PAGED, W_PAGED))
+def test_random_paged_prefill(rg, i):
+    draw = paged_draw(i, rg)
     print("paged prefill", draw, flush=True)
     window, scale = draw["window"], draw["scale"]
     case = wl.make_case(6, seed=draw["seed"], name="random_paged",
