@@ -2,6 +2,7 @@
 validation rejects bad arguments before any launch.  No GPU needed: every call
 here returns from validation without touching the HIP runtime's devices."""
 import ctypes
+import threading
 import os
 import re
 
@@ -224,3 +225,19 @@ def test_stream_probe_validation(lib):
     assert f(p, p, p, p, p, 2, 8, 64, 16, 4, 10, 64, 64, 0, 2, 1, None) == 2    # head_dim 64
     assert f(None, None, None, None, None, 2, 8, 128, 16, 4, 10, 64, 64, 0, 2, 1, None) == 1
     assert f(p, p, p, p, p, 0, 8, 128, 16, 4, 10, 64, 64, 0, 2, 1, None) == 0   # nothing to do
+
+
+def test_errors_stay_with_their_thread(lib):
+    # pa_last_error is per host thread: a failing call on one thread leaves the
+    # other thread's message alone
+    msgs = {}
+
+    def fail(tag, hd):
+        lib.paged_attention_reduce(None, None, None, None, None, 2, 8, hd, 512, 4, 1, None)
+        msgs[tag] = lib.pa_last_error().decode()
+
+    t1 = threading.Thread(target=fail, args=("a", 80))
+    t1.start()
+    t1.join()
+    fail("b", -1)
+    assert "head_dim 80" in msgs["a"] and "non-positive" in msgs["b"], msgs
