@@ -127,25 +127,96 @@ def prefill_cpu_baseline(pc, seconds):
                       f"BLAS threads {blas_threads()}, {host_note()}"}
 
 
-def decode_cpu_baseline(case, seconds, unique_bytes_per_kv_byte=1.0):
+def decode_cpu_baseline(case, seconds, unique_bytes_per_kv_byte=1.0, pools=None, window=0, kv8=False, seqs=None):
     """The fp64 oracle's decode of whole sequences of the same workload, in
-    order (cycling), until `seconds` have passed: GB/s of KV processed."""
+    order (cycling over the first `seqs`), until `seconds` have passed: GB/s of
+    the KV the queries see (the last `window` positions under a window; one
+    byte per element for an E4M3 pool).  `pools`: the (k, v) pools to read
+    when not the case's own (written on the host by the oracle)."""
     import oracle
     spec = case.spec
     B, Hkv, d = spec.batch, spec.num_kv_heads, spec.head_dim
+    kc, vc = pools if pools is not None else (case.k_cache, case.v_cache)
+    fp8 = dict(kv_dtype=oracle.E4M3, k_scale=case.k_scale, v_scale=case.v_scale) if kv8 else {}
+    per_pos = Hkv * 2 * d * (1 if kv8 else 2)
+    nseq = min(B, seqs) if seqs else B
     t0 = time.perf_counter()
     n, nbytes = 0, 0
     while time.perf_counter() - t0 < seconds:
-        b = n % B
-        oracle.decode(case.q[b:b + 1], case.k_cache, case.v_cache, case.block_tables[b:b + 1],
-                      case.context_lens[b:b + 1], spec.block_size, case.scale, spec.dtype)
+        b = n % nseq
+        oracle.decode(case.q[b:b + 1], kc, vc, case.block_tables[b:b + 1], case.context_lens[b:b + 1],
+                      spec.block_size, case.scale, spec.dtype, window=window, **fp8)
         n += 1
-        nbytes += int(case.context_lens[b]) * Hkv * 2 * d * 2
+        ctx = int(case.context_lens[b])
+        nbytes += (min(ctx, window) if window else ctx) * per_pos
     dt = time.perf_counter() - t0
     return {"value": round(nbytes * unique_bytes_per_kv_byte / dt / 1e9, 4), "unit": "GB/s",
             "cores": int(blas_threads()), "kind": "oracle",
             "sample": f"fp64 NumPy oracle decode of {n} sequences in order ({nbytes / 1e6:.1f} MB of KV) "
                       f"in {dt:.2f} s; BLAS threads {blas_threads()}, {host_note()}"}
+
+
+def window_cpu_baseline(case, window, seconds):
+    """The oracle's sliding-window decode of the window workload (its new
+    tokens written on the host first)."""
+    import oracle
+    kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping,
+                             case.spec.block_size)
+    return decode_cpu_baseline(case, seconds, pools=(kc, vc), window=window)
+
+
+def fp8_cpu_baseline(case, seconds, nseq=12):
+    """The oracle's decode over an E4M3 pool: the first `nseq` sequences'
+    history written by the oracle's FP8 write (not timed), then decoded in
+    order until `seconds` have passed."""
+    import oracle
+    tok = int(case.context_lens[:nseq].sum())   # the workload lists each sequence's positions in order
+    kc, vc = oracle.kv_write_fp8(case.k_cache, case.v_cache, case.k_new[:tok], case.v_new[:tok],
+                                 case.slot_mapping[:tok], case.spec.block_size, case.spec.dtype, case.k_scale,
+                                 case.v_scale)
+    r = decode_cpu_baseline(case, seconds, pools=(kc, vc), kv8=True, seqs=nseq)
+    r["sample"] += f" (the first {nseq} sequences, their E4M3 history written by the oracle beforehand)"
+    return r
+
+
+def paged_prefill_cpu_baseline(case, seconds):
+    """The oracle's paged prefill of whole sequences in order (the chunks'
+    K/V written on the host first): TFLOP/s over the GPU figure's count."""
+    import oracle
+    bs = case.spec.block_size
+    kc, vc = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, case.slot_mapping, bs)
+    lq = np.diff(case.cu_seqlens_q).astype(np.int64)
+    pre = case.context_lens.astype(np.int64) - lq
+    t0 = time.perf_counter()
+    done, fl = 0, 0.0
+    while time.perf_counter() - t0 < seconds and done < len(lq):
+        oracle.paged_prefill(case.q, kc, vc, case.block_tables, case.cu_seqlens_q, case.context_lens, bs, case.scale,
+                             case.spec.dtype, seqs=[done])
+        fl += 4.0 * case.spec.head_dim * case.spec.num_q_heads * float(lq[done] * pre[done] + lq[done] * (lq[done] + 1) // 2)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle paged prefill of the first {done} of {len(lq)} sequences "
+                      f"({int(lq[:done].sum())} query rows, all {case.spec.num_q_heads} heads) in {dt:.2f} s; "
+                      f"BLAS threads {blas_threads()}, {host_note()}"}
+
+
+def rope_cpu_baseline(pc, positions, rot_dim, base, bytes_per_token):
+    """The oracle's fused RoPE cache write over the prompt rows, once: GB/s of
+    the same algorithmic bytes per token as the GPU figure."""
+    from oracle import rope
+    from attention_paged_kv_write_amd import workloads as wl
+    spec = pc.spec
+    pool = wl.empty_pool(pc.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim, spec.dtype)
+    t0 = time.perf_counter()
+    rope.rope_kv_write(pc.q, pc.k, pc.v, pool, pool.copy(), pc.slot_mapping, positions, spec.block_size, rot_dim,
+                       base, spec.dtype)
+    dt = time.perf_counter() - t0
+    T = pc.total_tokens
+    return {"value": round(bytes_per_token * T / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads()),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle RoPE cache write of all {T} prompt rows once in {dt:.2f} s; "
+                      f"BLAS threads {blas_threads()}, {host_note()}"}
 
 
 def timed_groups(torch, stream, fn, n_items, n_groups, group=10):
@@ -567,6 +638,13 @@ def main(argv=None):
             if not args.no_cpu_baseline:
                 prefill["cpu_baseline"] = prefill_cpu_baseline(pc, args.cpu_seconds)
                 log(f"prefill cpu baseline {prefill['cpu_baseline']['value']} TFLOP/s")
+                try:
+                    rope_write["cpu_baseline"] = rope_cpu_baseline(
+                        pc, np.concatenate([np.arange(cu_h[i + 1] - cu_h[i]) for i in range(len(cu_h) - 1)])
+                        .astype(np.int32), d_, 10000.0, rope_bytes / T_)
+                    log(f"rope write cpu baseline {rope_write['cpu_baseline']['value']} GB/s")
+                except Exception as e:  # a baseline must not cost the GPU figures
+                    log(f"rope cpu baseline failed: {e!r}")
             del pq, pk, pv, pool, pool_v, pcopies, pools, wsrc
             torch.cuda.empty_cache()
 
@@ -607,6 +685,12 @@ def main(argv=None):
                              "tokens_per_s": round(cc.total_q / (cms * 1e-3), 1)}
             prefill["paged_prefill"] = paged_prefill
             log(f"paged prefill {cms * 1e3:.1f} us -> {ctf:.1f} TFLOP/s")
+            if not args.no_cpu_baseline:
+                try:
+                    paged_prefill["cpu_baseline"] = paged_prefill_cpu_baseline(cc, min(args.cpu_seconds, 5.0))
+                    log(f"paged prefill cpu baseline {paged_prefill['cpu_baseline']['value']} TFLOP/s")
+                except Exception as e:
+                    log(f"paged prefill cpu baseline failed: {e!r}")
 
             del ckc, cvc, cq, cout
             torch.cuda.empty_cache()
@@ -774,6 +858,12 @@ def main(argv=None):
                       "decode_tokens_per_s": round(wB / (float(np.mean(wstep_ms)) * 1e-3), 1),
                       "paged_prefill": None}
             log(f"window decode kernel {wavg * 1e3:.1f} us -> {wgbs:.0f} GB/s; step {np.mean(wstep_ms) * 1e3:.1f} us")
+            if not args.no_cpu_baseline:
+                try:
+                    window["cpu_baseline"] = window_cpu_baseline(wc, W, min(args.cpu_seconds, 5.0))
+                    log(f"window decode cpu baseline {window['cpu_baseline']['value']} GB/s")
+                except Exception as e:
+                    log(f"window cpu baseline failed: {e!r}")
             del wcopies
             torch.cuda.empty_cache()
 
@@ -913,6 +1003,12 @@ def main(argv=None):
                                 "algorithmic_bytes_per_launch": fbytes}}
             log(f"fp8 decode kernel {favg * 1e3:.1f} us -> {fgbs:.0f} GB/s of E4M3 KV; step {fsms * 1e3:.1f} us; "
                 f"history write ({fw_tokens} tokens) {fw_ms * 1e3:.1f} us -> {fw_bytes / (fw_ms * 1e-3) / 1e9:.0f} GB/s")
+            if not args.no_cpu_baseline:
+                try:
+                    fp8["cpu_baseline"] = fp8_cpu_baseline(fc, min(args.cpu_seconds, 5.0))
+                    log(f"fp8 decode cpu baseline {fp8['cpu_baseline']['value']} GB/s")
+                except Exception as e:
+                    log(f"fp8 cpu baseline failed: {e!r}")
             del fcopies
             torch.cuda.empty_cache()
     except Exception as e:  # a failing secondary figure must not cost the headline line
