@@ -639,9 +639,8 @@ def main(argv=None):
                 prefill["cpu_baseline"] = prefill_cpu_baseline(pc, args.cpu_seconds)
                 log(f"prefill cpu baseline {prefill['cpu_baseline']['value']} TFLOP/s")
                 try:
-                    rope_write["cpu_baseline"] = rope_cpu_baseline(
-                        pc, np.concatenate([np.arange(cu_h[i + 1] - cu_h[i]) for i in range(len(cu_h) - 1)])
-                        .astype(np.int32), d_, 10000.0, rope_bytes / T_)
+                    rope_write["cpu_baseline"] = rope_cpu_baseline(pc, rpos.cpu().numpy(), d_, 10000.0,
+                                                                   rope_bytes / T_)
                     log(f"rope write cpu baseline {rope_write['cpu_baseline']['value']} GB/s")
                 except Exception as e:  # a baseline must not cost the GPU figures
                     log(f"rope cpu baseline failed: {e!r}")
