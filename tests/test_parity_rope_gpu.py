@@ -160,3 +160,23 @@ def test_decode_over_rope_written_cache():
     qr, kr, okc, ovc = rope.rope_kv_write(q_rows, k, v, pool, pool.copy(), slots, pos, bs, d, BASE, wl.BF16)
     ref_out, ref_lse = oracle.decode(qr[last], okc, ovc, tables, ctx, bs, 1 / np.sqrt(d), wl.BF16)
     assert_parity(to_host_f64(out), to_host_f64(lse), ref_out, ref_lse, wl.BF16, "decode after fused RoPE write")
+
+
+def test_fused_rope_write_workload_full_size():
+    """All of workload 3's prompt rows (16 sequences, 17,202 rows at its seed)
+    in the benchmark's launch configuration: bf16, rot_dim = head_dim, a table
+    of max_seqlen positions.  Every rotated element within the bar; the pool
+    holds exactly the in-place k and the input v at each slot, NaN elsewhere."""
+    case = wl.make_case(3)
+    d, bs = case.spec.head_dim, case.spec.block_size
+    (dq, dk, kc, vc), (qr, kr, _, _), pos = run_fused(case, wl.BF16, d, P=case.max_seqlen)
+    check_rotated(dq, qr, case.q, pos, d, wl.BF16, "q")
+    check_rotated(dk, kr, case.k, pos, d, wl.BF16, "k")
+    slots = case.slot_mapping.astype(np.int64)
+    assert (slots >= 0).all()
+    want_k = wl.empty_pool(case.num_blocks, case.spec.num_kv_heads, bs, d, wl.BF16)
+    want_v = want_k.copy()
+    want_k[slots // bs, :, slots % bs] = to_host_bits(dk)
+    want_v[slots // bs, :, slots % bs] = case.v
+    np.testing.assert_array_equal(to_host_bits(kc), want_k)
+    np.testing.assert_array_equal(to_host_bits(vc), want_v)
